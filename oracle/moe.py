@@ -1,0 +1,136 @@
+"""The five-stage NVFP4 mixture-of-experts expert layer (test infrastructure).
+
+Stages as the pages list them (DEBUG_LOG, "NVFP4 MoE Pipeline"):
+
+1. ``stage_activation(hidden)``: quantize x with the NVFP4 rule (oracle.quantize),
+   one global scale gs1 over all of x;
+2. token-to-expert permutation: one slot per (token t, choice j) whose expert id
+   lies in [0, E); ids outside that range are skipped (the pages do not define
+   them; this is the reading taken);
+3. L1 GEMM of each slot's quantized row against w13[e] = [gate; up] with
+   alpha = gs1 * w13_alpha[e]; gate is the first I output columns, up the last I
+   (src commit log, gate/up interleave removal);
+4. act = SiLU(gate) * up, then ``stage_activation(act)``: one global scale gs2
+   over the activations of all valid slots;
+5. L2 GEMM with alpha = gs2 * w2_alpha[e], then "scatter with routing weights":
+   y[t] = sum_j topk_weights[t, j] * out[t, j] in j order.
+
+Rounding points (the pages print bf16-looking intermediates and say "bf16 out";
+readings in the design doc): gate_up is rounded to bf16 before SiLU (R1); act is
+rounded to bf16 once (R2); nothing between the L2 sum and y is rounded except
+the single final bf16 rounding of y (R3). Everything else here is float64, and
+SiLU(z) = z / (1 + exp(-z)).
+
+Parity: each stage is pinned through the modules it calls (formats, quantize,
+gemm). The layer's end-to-end values have no published expected value (the
+pages never reach a correct layer output): PARITY UNPINNED end to end; the
+composition is checked by the invariants in tests/test_oracle_moe.py
+(gate/up split, per-expert alpha, skipped slots, slot-order independence, the
+pure-Python twin on the tiny layer).
+"""
+import numpy as np
+
+from .formats import bf16_from_f64, bf16_to_f32
+from .quantize import (dequantize_cols, dequantize_rows, quantize_bf16,
+                       quantize_f32)
+
+
+def silu(z):
+    """z * sigmoid(z) = z / (1 + exp(-z)), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def slots_by_expert(topk_ids, num_experts):
+    """For each expert, the (token, choice) pairs routed to it, in (t, j) order."""
+    ids = np.asarray(topk_ids)
+    out = []
+    for e in range(num_experts):
+        t_idx, j_idx = np.nonzero(ids == e)
+        out.append((t_idx, j_idx))
+    return out
+
+
+def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
+                w2q, w2sf, w2_alpha, keep=False):
+    """Reference layer output.
+
+    Shapes: x_bits (T, H) uint16 bf16 bits; topk_ids (T, k) int; topk_weights
+    (T, k) float32; w13q (E, H/2, 2I) uint8; w13sf (E, H/16, 2I) uint8;
+    w13_alpha (E,) float32; w2q (E, I/2, H); w2sf (E, I/16, H); w2_alpha (E,).
+
+    Returns a dict with y (float64, unrounded), y_bits (bf16) and, when keep is
+    set, the per-slot intermediates indexed [t, j]: gu (float64, unrounded),
+    act_bits (bf16, T x k x I), aq, asf, contrib (weighted L2 rows, float64),
+    valid mask, plus xq, xsf, gs1, gs2.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    ids = np.asarray(topk_ids).astype(np.int64)
+    wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
+    T, H = x_bits.shape
+    k = ids.shape[1] if ids.ndim == 2 else 0
+    E = w13q.shape[0]
+    I = w2q.shape[1] * 2
+
+    # stage 1
+    xq, xsf, gs1 = quantize_bf16(x_bits)
+
+    # stage 2
+    groups = slots_by_expert(ids, E)
+    valid = (ids >= 0) & (ids < E)
+
+    # stage 3 + the SiLU half of stage 4
+    act_bits = np.zeros((T, k, I), dtype=np.uint16)
+    gu_keep = np.zeros((T, k, 2 * I), dtype=np.float64) if keep else None
+    for e, (t_idx, j_idx) in enumerate(groups):
+        if t_idx.size == 0:
+            continue
+        a = dequantize_rows(xq[t_idx], xsf[t_idx])
+        b = dequantize_cols(w13q[e], w13sf[e])
+        alpha = np.float64(gs1) * np.float64(np.float32(w13_alpha[e]))
+        gu_f64 = alpha * (a @ b)
+        if keep:
+            gu_keep[t_idx, j_idx] = gu_f64
+        gu = bf16_from_f64(gu_f64)                                   # R1
+        g = bf16_to_f32(gu[:, :I]).astype(np.float64)
+        u = bf16_to_f32(gu[:, I:]).astype(np.float64)
+        act_bits[t_idx, j_idx] = bf16_from_f64(silu(g) * u)          # R2
+
+    # the requantization half of stage 4: one gs2 over all valid slots
+    t_all, j_all = np.nonzero(valid)
+    aq = np.zeros((T, k, I // 2), dtype=np.uint8)
+    asf = np.zeros((T, k, I // 16), dtype=np.uint8)
+    if t_all.size:
+        q_v, sf_v, gs2 = quantize_bf16(act_bits[t_all, j_all])
+        aq[t_all, j_all] = q_v
+        asf[t_all, j_all] = sf_v
+    else:
+        gs2 = np.float32(0.0)
+
+    # stage 5: L2 and the weighted combine, float64 until the final rounding
+    y = np.zeros((T, H), dtype=np.float64)
+    contrib = np.zeros((T, k, H), dtype=np.float64)
+    for e, (t_idx, j_idx) in enumerate(groups):
+        if t_idx.size == 0:
+            continue
+        a = dequantize_rows(aq[t_idx, j_idx], asf[t_idx, j_idx])
+        b = dequantize_cols(w2q[e], w2sf[e])
+        alpha = np.float64(gs2) * np.float64(np.float32(w2_alpha[e]))
+        contrib[t_idx, j_idx] = wts[t_idx, j_idx][:, None] * (alpha * (a @ b))
+    for j in range(k):                                               # j order
+        y += contrib[:, j, :]
+    out = {"y": y, "y_bits": bf16_from_f64(y), "gs1": gs1, "gs2": np.float32(gs2)}
+    if keep:
+        out.update(xq=xq, xsf=xsf, gu=gu_keep, act_bits=act_bits, aq=aq, asf=asf,
+                   valid=valid, contrib=contrib)
+    return out
+
+
+def quantize_act_rows(act_bits):
+    """Stage-4 quantization on its own: rows of bf16 activations."""
+    return quantize_bf16(act_bits)
+
+
+__all__ = ["moe_forward", "silu", "slots_by_expert", "quantize_act_rows",
+           "quantize_f32"]

@@ -1,0 +1,124 @@
+"""NVFP4 two-level quantization and dequantization (test infrastructure).
+
+Follows the rule the pages give for the weight loader and for
+``stage_activation`` (DEBUG_LOG, Hypothesis 6 steps 1-5 and "NVFP4 MoE
+Pipeline"; DEBUG_LOG revision, "input_scale red herring"; src commit log,
+quantizer fix and E4M3 `.view` fix):
+
+1. global scale  gs = amax / (6 * 448), amax over the whole tensor;
+2. block scale   s  = block_amax / (6 * gs), one per 16 consecutive elements
+                      along the reduction axis, stored as an E4M3 byte;
+3. element       nearest E2M1 value of x / (s_stored * gs);
+4. packing       element 2j in the low nibble, element 2j+1 in the high one.
+
+The pages leave the arithmetic open. This oracle takes the plainest reading and
+every GPU path must follow the same one (the readings are listed in the design doc):
+
+* all of it is IEEE float32 with round-to-nearest-even, no fused multiply-add,
+  in exactly this order: gs = fl(amax / 2688); six_gs = fl(6 * gs);
+  s = fl(bmax / six_gs), clamped to 448; den = fl(s_stored * gs);
+  v = fl(|x| / den);
+* the element divides by the *stored* (decoded) block scale: the stored byte is
+  "the actual dequant factor" (src commit log, quantizer fix item 2);
+* gs == 0 gives scale 0; den == 0 gives magnitude 0;
+* the nibble's sign bit is the sign bit of x, also for -0.0 and for negative
+  values that round to magnitude 0.
+
+Parity pins (tests/test_oracle_quantize.py): the block holding the tensor amax
+always gets scale byte 0x7E and its amax element magnitude 6.0 (closed form);
+the pages' own (amax, global scale) pairs 3.86 -> 1.4e-3 and 2.86e-4 -> 0.77
+(tests/golden/global_scale_pairs.txt); nibble order; sign symmetry Q(-x);
+power-of-two invariance Q(2^j x); the round-trip error bound; bit-for-bit
+agreement with the exact-rational twin in ``oracle.loops``.
+"""
+import numpy as np
+
+from .formats import (bf16_to_f32, e2m1_decode, e2m1_encode_magnitude,
+                      e4m3_decode, e4m3_encode_nonneg)
+
+F32 = np.float32
+SIX_TIMES_E4M3_MAX = F32(2688.0)   # 6 * 448, exact
+BLOCK = 16
+
+
+def global_scale(amax):
+    """gs = fl32(amax / 2688)."""
+    return F32(F32(amax) / SIX_TIMES_E4M3_MAX)
+
+
+def quantize_f32(x):
+    """Quantize a float32 matrix (rows, cols), blocks of 16 along cols.
+
+    Returns (q uint8 (rows, cols/2), sf uint8 (rows, cols/16), gs float32).
+    """
+    x = np.asarray(x, dtype=F32)
+    if x.ndim != 2 or x.shape[1] % BLOCK:
+        raise ValueError("quantize expects a 2-D array with cols % 16 == 0")
+    rows, cols = x.shape
+    ax = np.abs(x)
+    amax = F32(ax.max()) if x.size else F32(0.0)
+    gs = global_scale(amax)
+    six_gs = F32(F32(6.0) * gs)
+
+    bmax = ax.reshape(rows, cols // BLOCK, BLOCK).max(axis=2)
+    if gs > 0:
+        s = (bmax / six_gs).astype(F32)
+        s = np.minimum(s, F32(448.0))
+    else:
+        s = np.zeros_like(bmax)
+    sf = e4m3_encode_nonneg(s)
+    s_dec = e4m3_decode(sf).astype(F32)                 # exact in float32
+    den = (s_dec * gs).astype(F32)
+
+    den_e = np.repeat(den, BLOCK, axis=1)
+    ok = den_e > 0
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        v = np.where(ok, ax / np.where(ok, den_e, F32(1.0)), F32(0.0)).astype(F32)
+    mag = e2m1_encode_magnitude(v)
+    nib = (np.signbit(x).astype(np.uint8) << 3) | mag
+    q = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    return q, sf.astype(np.uint8), gs
+
+
+def quantize_bf16(x_bits):
+    """O-Q on bf16 input bits (uint16, rows x cols)."""
+    return quantize_f32(bf16_to_f32(x_bits))
+
+
+def quantize_weight_bf16(w_bits):
+    """Weight rule: W (K, N) bf16 bits, blocks of 16 along K, amax over all of W.
+
+    Returns (q (K/2, N), sf (K/16, N), alpha) with byte [kh, n] holding
+    W[2kh, n] in its low nibble and W[2kh+1, n] in its high nibble, i.e. the
+    activation rule applied to W transposed and stored transposed back.
+    """
+    q_t, sf_t, gs = quantize_bf16(np.ascontiguousarray(np.asarray(w_bits).T))
+    return np.ascontiguousarray(q_t.T), np.ascontiguousarray(sf_t.T), gs
+
+
+def unpack_nibbles(q, axis):
+    """Split packed bytes into nibbles along `axis`: low nibble first."""
+    q = np.asarray(q, dtype=np.uint8)
+    lo = q & 0xF
+    hi = q >> 4
+    st = np.stack([lo, hi], axis=axis + 1)
+    shape = list(q.shape)
+    shape[axis] *= 2
+    return st.reshape(shape)
+
+
+def dequantize_rows(q, sf):
+    """Row-blocked operand (rows, cols/2) + (rows, cols/16) -> float64 values.
+
+    The value excludes the global scale, which the GEMM applies through alpha.
+    """
+    nib = unpack_nibbles(q, axis=1)
+    scale = np.repeat(e4m3_decode(sf), BLOCK, axis=1)
+    return e2m1_decode(nib) * scale
+
+
+def dequantize_cols(q, sf):
+    """K-packed operand (K/2, N) + (K/16, N) -> float64 (K, N), gs excluded."""
+    nib = unpack_nibbles(q, axis=0)
+    scale = np.repeat(e4m3_decode(sf), BLOCK, axis=0)
+    return e2m1_decode(nib) * scale

@@ -1,0 +1,152 @@
+"""Pins and invariants of the oracle's expert layer (O-M)."""
+import time
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import loops
+from oracle.formats import bf16_to_f32
+from oracle.moe import moe_forward
+from oracle.quantize import quantize_weight_bf16
+
+
+def make_layer(cfg):
+    """Oracle-side inputs of a layer config: weights quantized with O-Q."""
+    x = W.activations(cfg)
+    ids, wts = W.routing(cfg)
+    w13q, w13sf, w13a, w2q, w2sf, w2a = [], [], [], [], [], []
+    for e in range(cfg.E):
+        w13, w2 = W.expert_weights_bf16(cfg, e)
+        q, sf, a = quantize_weight_bf16(w13)
+        w13q.append(q); w13sf.append(sf); w13a.append(a)
+        q, sf, a = quantize_weight_bf16(w2)
+        w2q.append(q); w2sf.append(sf); w2a.append(a)
+    w13a = np.array(w13a, np.float32)
+    w2a = np.array(w2a, np.float32)
+    if cfg.alpha_loguniform:
+        w13a, w2a = W.alphas_loguniform(cfg)
+    return dict(x=x, ids=ids, wts=wts, w13q=np.stack(w13q), w13sf=np.stack(w13sf),
+                w13a=w13a, w2q=np.stack(w2q), w2sf=np.stack(w2sf), w2a=w2a)
+
+
+def run(L, **over):
+    d = dict(L)
+    d.update(over)
+    return moe_forward(d["x"], d["ids"], d["wts"], d["w13q"], d["w13sf"], d["w13a"],
+                       d["w2q"], d["w2sf"], d["w2a"], keep=True)
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return make_layer(W.TINY)
+
+
+def test_vectorized_layer_matches_exact_twin_on_tiny_config(tiny):
+    # "A wrong reference is worse than no reference" (DEBUG_LOG revision): the
+    # NumPy oracle must agree bit for bit with the exact-rational twin before it
+    # is trusted against any GPU result
+    L = tiny
+    t0 = time.time()
+    ref = run(L)
+    tw = loops.moe_forward(L["x"].tolist(), L["ids"].tolist(), L["wts"].tolist(),
+                           L["w13q"].tolist(), L["w13sf"].tolist(), L["w13a"].tolist(),
+                           L["w2q"].tolist(), L["w2sf"].tolist(), L["w2a"].tolist())
+    assert float(ref["gs1"]) == tw["gs1"]
+    assert float(ref["gs2"]) == tw["gs2"]
+    for (t, j), bits in tw["act_bits"].items():
+        assert (ref["act_bits"][t, j] == np.array(bits, np.uint16)).all()
+        assert (ref["aq"][t, j] == np.array(tw["aq"][(t, j)], np.uint8)).all()
+        assert (ref["asf"][t, j] == np.array(tw["asf"][(t, j)], np.uint8)).all()
+    assert (ref["y_bits"] == np.array(tw["y_bits"], np.uint16)).all()
+    assert time.time() - t0 < 120
+
+
+def test_per_expert_alpha_scales_only_its_rows(tiny):
+    # src commit log, per-expert global scale fix: each expert uses its own alpha.
+    # Doubling w13_alpha[e] doubles exactly the gate_up rows of expert e's slots.
+    L = tiny
+    base = run(L)
+    for e in range(W.TINY.E):
+        a2 = L["w13a"].copy()
+        a2[e] *= 2
+        out = run(L, w13a=a2)
+        mine = L["ids"] == e
+        assert (out["gu"][mine] == 2 * base["gu"][mine]).all()
+        assert (out["gu"][~mine] == base["gu"][~mine]).all()
+
+
+def test_gate_up_split_is_plain_concat(tiny):
+    # src commit log, interleave removal: w13 = [gate; up] along the output dim.
+    # Zeroing the up half (scale bytes 0) makes every activation zero and y zero.
+    L = tiny
+    I = W.TINY.I
+    sf = L["w13sf"].copy()
+    sf[:, :, I:] = 0
+    out = run(L, w13sf=sf)
+    assert ((out["act_bits"] & 0x7FFF) == 0).all()
+    assert (out["y"] == 0).all()
+    # zeroing the gate half does the same (SiLU(0) = 0)
+    sf = L["w13sf"].copy()
+    sf[:, :, :I] = 0
+    assert (run(L, w13sf=sf)["y"] == 0).all()
+    # swapping the halves changes y (SiLU is not symmetric)
+    sw_q = np.concatenate([L["w13q"][:, :, I:], L["w13q"][:, :, :I]], axis=2)
+    sw_sf = np.concatenate([L["w13sf"][:, :, I:], L["w13sf"][:, :, :I]], axis=2)
+    base = run(L)
+    sw = run(L, w13q=sw_q, w13sf=sw_sf)
+    assert np.abs(sw["y"] - base["y"]).max() > 1e-3 * np.abs(base["y"]).max()
+
+
+def test_token_order_independence(tiny):
+    # per-token results do not depend on where the token sits in the batch
+    L = tiny
+    perm = np.random.default_rng(3).permutation(W.TINY.T)
+    base = run(L)
+    out = run(L, x=L["x"][perm], ids=L["ids"][perm], wts=L["wts"][perm])
+    assert (out["y_bits"] == base["y_bits"][perm]).all()
+    assert out["gs1"] == base["gs1"] and out["gs2"] == base["gs2"]
+
+
+def test_skipped_slots(tiny):
+    # ids outside [0, E) contribute nothing; a token with every slot skipped
+    # gets y = 0; other tokens keep their exact values while gs2 is unchanged
+    L = tiny
+    base = run(L)
+    ids = L["ids"].copy()
+    ids[3, :] = -1
+    ids[5, 1] = W.TINY.E + 7
+    out = run(L, ids=ids)
+    assert (out["y"][3] == 0).all()
+    if out["gs2"] == base["gs2"]:
+        keep = np.ones(W.TINY.T, bool)
+        keep[[3, 5]] = False
+        assert (out["y_bits"][keep] == base["y_bits"][keep]).all()
+    assert (out["act_bits"][5, 0] == base["act_bits"][5, 0]).all()
+    # all slots skipped: y = 0, gs2 = 0
+    out = run(L, ids=np.full_like(ids, -1))
+    assert (out["y"] == 0).all() and out["gs2"] == 0
+
+
+def test_combine_is_weighted_sum_of_l2_rows(tiny):
+    # "scatter with routing weights": y[t] = sum_j w[t,j] * out[t,j]
+    L = tiny
+    out = run(L)
+    assert np.allclose(out["y"], out["contrib"].sum(axis=1), rtol=1e-14, atol=0)
+    w2 = L["wts"].copy()
+    w2[:, 1] = 0
+    out2 = run(L, wts=w2)
+    assert (out2["y"] == out["contrib"][:, 0, :]).all()
+
+
+def test_act_is_silu_gate_times_up_of_rounded_gate_up(tiny):
+    L = tiny
+    I = W.TINY.I
+    out = run(L)
+    from oracle.formats import bf16_from_f64
+    gu = bf16_to_f32(bf16_from_f64(out["gu"])).astype(np.float64)
+    g, u = gu[..., :I], gu[..., I:]
+    ref = g * (1.0 / (1.0 + np.exp(-g))) * u
+    act = bf16_to_f32(out["act_bits"]).astype(np.float64)
+    valid = out["valid"]
+    assert np.allclose(act[valid], ref[valid], rtol=2.0 ** -8, atol=1e-30)
