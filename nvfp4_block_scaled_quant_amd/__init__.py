@@ -1,0 +1,250 @@
+"""Python binding of libnvfp4moe (NVFP4 expert layer on MI355X / gfx950).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch provides device memory and the current stream. The functions
+mirror the C ABI in include/nvfp4moe.h:
+
+    quantize(x)                      -> (q, sf, gs)
+    quantize_weights(w)              -> (q, sf, alpha)
+    gemm(aq, asf, a_gs, bq, bsf, b_alpha) -> out (bf16)
+    moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
+                w2, w2_sf, w2_alpha, workspace=None, stage_events=None) -> y
+
+The library must be built in-tree first (``python -m
+nvfp4_block_scaled_quant_amd.build``); importing this package without it
+raises ImportError, so no caller can silently fall back to anything else.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4moe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m nvfp4_block_scaled_quant_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+
+_SIGS = {
+    "nvfp4_strerror": ([_int], ctypes.c_char_p),
+    "nvfp4_version": ([], _int),
+    "nvfp4_quantize_workspace": ([_i64, _i64], _sz),
+    "nvfp4_quantize": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_quantize_weights_workspace": ([_i64, _i64, _i64], _sz),
+    "nvfp4_quantize_weights": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_gemm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_moe_workspace": ([_i64, _i64, _i64, _i64, _i64], _sz),
+    "nvfp4_moe_workspace_layout": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
+    "nvfp4_moe_forward": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _sz, _vp, _vp], _int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+# stage / workspace indices (include/nvfp4moe.h)
+STAGES = ("route", "quant_x", "l1", "requant", "l2", "combine")
+NUM_EVENTS = len(STAGES) + 1
+WS_NAMES = ("xq", "xsf", "gs1", "gs2", "counts", "offsets", "sorted_slot", "slot_row",
+            "act", "aq", "asf", "o2")
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status, where):
+        msg = _lib.nvfp4_strerror(status).decode()
+        super().__init__(f"{where}: status {status} ({msg})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != 0:
+        raise Nvfp4Error(status, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, dim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def version():
+    v = _lib.nvfp4_version()
+    return (v >> 16, v & 0xFFFF)
+
+
+def strerror(status):
+    return _lib.nvfp4_strerror(status).decode()
+
+
+def quantize(x, q=None, sf=None, gs=None, workspace=None):
+    """NVFP4-quantize a bf16 (M, K) activation. Returns (q uint8 (M, K/2),
+    sf uint8 (M, K/16) E4M3 bits, gs float32 (1,))."""
+    _need(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    sf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    gs = torch.empty((1,), dtype=torch.float32, device=dev) if gs is None else gs
+    nws = _lib.nvfp4_quantize_workspace(M, K)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _check(_lib.nvfp4_quantize(_ptr(x), M, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
+                               ws.numel(), _stream()), "nvfp4_quantize")
+    return q, sf, gs
+
+
+def quantize_weights(w):
+    """Quantize E bf16 weight matrices W[e] (K, N) with blocks along K.
+    Returns (q uint8 (E, K/2, N), sf uint8 (E, K/16, N), alpha float32 (E,))."""
+    _need(w, torch.bfloat16, "w", 3)
+    E, K, N = w.shape
+    dev = w.device
+    q = torch.empty((E, K // 2, N), dtype=torch.uint8, device=dev)
+    sf = torch.empty((E, K // 16, N), dtype=torch.uint8, device=dev)
+    alpha = torch.empty((E,), dtype=torch.float32, device=dev)
+    nws = _lib.nvfp4_quantize_weights_workspace(E, K, N)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    _check(_lib.nvfp4_quantize_weights(_ptr(w), E, K, N, _ptr(q), _ptr(sf), _ptr(alpha), _ptr(ws),
+                                       ws.numel(), _stream()), "nvfp4_quantize_weights")
+    return q, sf, alpha
+
+
+def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
+    """Block-scaled NVFP4 GEMM: (M, K/2)+(M, K/16) x (K/2, N)+(K/16, N) -> bf16 (M, N)."""
+    for t, n, d in ((aq, "aq", torch.uint8), (asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
+                    (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
+                    (b_alpha, "b_alpha", torch.float32)):
+        _need(t, d, n)
+    M = aq.shape[0]
+    K = aq.shape[1] * 2
+    N = bq.shape[1]
+    if bq.shape[0] * 2 != K or asf.shape != (M, K // 16) or bsf.shape != (K // 16, N):
+        raise ValueError("operand shapes do not match")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device) if out is None else out
+    _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),
+                           M, N, K, _ptr(out), _stream()), "nvfp4_gemm")
+    return out
+
+
+def moe_workspace_size(T, H, I, E, topk):
+    n = _lib.nvfp4_moe_workspace(T, H, I, E, topk)
+    if n == 0:
+        raise Nvfp4Error(2, "nvfp4_moe_workspace")
+    return n
+
+
+def moe_workspace_layout(T, H, I, E, topk):
+    arr = (_sz * len(WS_NAMES))()
+    _check(_lib.nvfp4_moe_workspace_layout(T, H, I, E, topk, arr), "nvfp4_moe_workspace_layout")
+    return dict(zip(WS_NAMES, list(arr)))
+
+
+def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
+                y=None, workspace=None, stage_events=None):
+    """The five-stage NVFP4 expert layer. Shapes as in include/nvfp4moe.h.
+
+    stage_events: None or a StageEvents; returns y (T, H) bf16.
+    """
+    _need(x, torch.bfloat16, "x", 2)
+    _need(topk_ids, torch.int32, "topk_ids", 2)
+    _need(topk_weights, torch.float32, "topk_weights", 2)
+    for t, n, d in ((w13, "w13", 3), (w13_sf, "w13_sf", 3), (w2, "w2", 3), (w2_sf, "w2_sf", 3)):
+        _need(t, torch.uint8, n, d)
+    _need(w13_alpha, torch.float32, "w13_alpha", 1)
+    _need(w2_alpha, torch.float32, "w2_alpha", 1)
+    T, H = x.shape
+    topk = topk_ids.shape[1]
+    E = w13.shape[0]
+    I = w2.shape[1] * 2
+    if (w13.shape != (E, H // 2, 2 * I) or w13_sf.shape != (E, H // 16, 2 * I)
+            or w2.shape != (E, I // 2, H) or w2_sf.shape != (E, I // 16, H)
+            or w13_alpha.shape != (E,) or w2_alpha.shape != (E,)
+            or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
+        raise ValueError("moe_forward: inconsistent shapes")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if y is None else y
+    nws = moe_workspace_size(T, H, I, E, topk)
+    if workspace is None:
+        workspace = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    ev = stage_events.handles if stage_events is not None else None
+    _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
+                                  _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
+                                  _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
+                                  workspace.numel(), _stream(), ev), "nvfp4_moe_forward")
+    return y
+
+
+class _Hip:
+    """The few HIP runtime calls the stage timer needs (events)."""
+    _rt = None
+
+    @classmethod
+    def rt(cls):
+        if cls._rt is None:
+            rt = ctypes.CDLL("libamdhip64.so")
+            rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+
+class StageEvents:
+    """HIP events recorded by nvfp4_moe_forward around each stage (on the
+    stream the stage's kernels run on)."""
+
+    def __init__(self, n=NUM_EVENTS):
+        rt = _Hip.rt()
+        self._arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._arr[i] = h
+        self.n = n
+
+    @property
+    def handles(self):
+        return ctypes.cast(self._arr, ctypes.c_void_p)
+
+    def elapsed_ms(self):
+        """Per-stage milliseconds of the last recorded forward."""
+        rt = _Hip.rt()
+        if rt.hipEventSynchronize(self._arr[self.n - 1]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = []
+        for i in range(self.n - 1):
+            ms = ctypes.c_float()
+            if rt.hipEventElapsedTime(ctypes.byref(ms), self._arr[i], self._arr[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return dict(zip(STAGES, out))
+
+    def __del__(self):
+        try:
+            rt = _Hip.rt()
+            for i in range(self.n):
+                rt.hipEventDestroy(self._arr[i])
+        except Exception:
+            pass

@@ -1,0 +1,302 @@
+// C ABI of the NVFP4 expert-layer library: argument validation, workspace
+// carving and the launch sequence. Declarations and contracts: include/nvfp4moe.h.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/nvfp4moe.h"
+#include "launch.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// 0 = not checked, 1 = gfx950, 2 = other
+std::atomic<int> g_device_ok[64];
+
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NVFP4_EHIP;
+    if (dev < 0 || dev >= 64) return NVFP4_EDEVICE;
+    int st = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NVFP4_EHIP;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? NVFP4_OK : NVFP4_EDEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+#define NVFP4_TRY(expr)                      \
+    do {                                     \
+        hipError_t e_ = (expr);              \
+        if (e_ != hipSuccess) return NVFP4_EHIP; \
+    } while (0)
+
+struct MoeLayout {
+    size_t off[NVFP4_MOE_WS_NUM];
+    size_t amax;        // 2 x uint32: x amax, act amax
+    size_t tiles;
+    size_t num_tiles;
+    size_t total;
+    int64_t max_tiles;
+};
+
+int64_t moe_max_tiles(int64_t S, int64_t E) {
+    if (S <= 0) return 0;
+    return S / kGemmBM + (E < S ? E : S);
+}
+
+MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+    MoeLayout L;
+    const int64_t S = T * topk;
+    const size_t sizes[NVFP4_MOE_WS_NUM] = {
+        (size_t)(T * H / 2),  (size_t)(T * H / 16), 4, 4,
+        (size_t)(4 * E),      (size_t)(4 * (E + 1)), (size_t)(4 * S), (size_t)(4 * S),
+        (size_t)(2 * S * I),  (size_t)(S * I / 2),  (size_t)(S * I / 16), (size_t)(4 * S * H)};
+    size_t cur = 0;
+    for (int i = 0; i < NVFP4_MOE_WS_NUM; ++i) {
+        L.off[i] = cur;
+        cur = align_up(cur + sizes[i]);
+    }
+    L.amax = cur;
+    cur = align_up(cur + 8);
+    L.max_tiles = moe_max_tiles(S, E);
+    L.tiles = cur;
+    cur = align_up(cur + sizeof(Tile) * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
+    L.num_tiles = cur;
+    cur = align_up(cur + 4);
+    L.total = cur;
+    return L;
+}
+
+bool moe_shape_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return false;
+    if (H % 16 || I % 16 || topk > E || E > kMaxExperts) return false;
+    if (T > (int64_t)1 << 24 || H > (int64_t)1 << 20 || I > (int64_t)1 << 20) return false;
+    if (T * topk >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_strerror(int status) {
+    switch (status) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_EINVAL: return "invalid argument (null or misaligned pointer, negative size)";
+        case NVFP4_ESHAPE: return "unsupported shape (K dimensions must be multiples of 16, 1 <= topk <= E <= 512)";
+        case NVFP4_EWORKSPACE: return "workspace missing, misaligned (256 bytes) or too small";
+        case NVFP4_EHIP: return "HIP runtime error or kernel launch failure";
+        case NVFP4_EDEVICE: return "current device is not an MI355X-class gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+int nvfp4_version(void) { return (1 << 16) | 0; }
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
+    (void)M;
+    (void)K;
+    return kAlign;
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* sf, float* gs,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (M < 0 || K <= 0) return NVFP4_EINVAL;
+    if (K % 16) return NVFP4_ESHAPE;
+    if (!gs || (M > 0 && (!x || !q || !sf))) return NVFP4_EINVAL;
+    if (M > 0 && (!aligned(x, 16) || !aligned(q, 8))) return NVFP4_EINVAL;
+    if (!aligned(gs, 4)) return NVFP4_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < nvfp4_quantize_workspace(M, K))
+        return NVFP4_EWORKSPACE;
+    int dv = check_device();
+    if (dv) return dv;
+    uint32_t* slot = static_cast<uint32_t*>(workspace);
+    NVFP4_TRY(launch_zero_u32(slot, 1, stream));
+    NVFP4_TRY(launch_amax_bf16(x, M * K, slot, stream));
+    NVFP4_TRY(launch_quant_rows(x, M, K, nullptr, slot, q, sf, gs, stream));
+    return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_quantize_weights_workspace(int64_t E, int64_t K, int64_t N) {
+    (void)K;
+    (void)N;
+    return align_up((size_t)(E > 0 ? E : 1) * 4);
+}
+
+int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N, uint8_t* q,
+                           uint8_t* sf, float* alpha, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (E < 0 || K <= 0 || N <= 0) return NVFP4_EINVAL;
+    if (K % 16 || E > 65535) return NVFP4_ESHAPE;
+    if (E == 0) return NVFP4_OK;
+    if (!w || !q || !sf || !alpha) return NVFP4_EINVAL;
+    if (!aligned(w, 16) || !aligned(alpha, 4)) return NVFP4_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign) ||
+        workspace_bytes < nvfp4_quantize_weights_workspace(E, K, N))
+        return NVFP4_EWORKSPACE;
+    int dv = check_device();
+    if (dv) return dv;
+    uint32_t* slots = static_cast<uint32_t*>(workspace);
+    NVFP4_TRY(launch_zero_u32(slots, (int)E, stream));
+    NVFP4_TRY(launch_amax_bf16_batched(w, E, K * N, slots, stream));
+    NVFP4_TRY(launch_quant_cols(w, E, K, N, slots, q, sf, alpha, stream));
+    return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
+int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const uint8_t* bq,
+               const uint8_t* bsf, const float* b_alpha, int64_t M, int64_t N, int64_t K,
+               uint16_t* out, hipStream_t stream) {
+    if (M < 0 || N <= 0 || K <= 0) return NVFP4_EINVAL;
+    if (K % 16 || N % 16) return NVFP4_ESHAPE;
+    if (M == 0) return NVFP4_OK;
+    if (!aq || !asf || !a_gs || !bq || !bsf || !b_alpha || !out) return NVFP4_EINVAL;
+    if (!aligned(aq, 8) || !aligned(bq, 4) || !aligned(bsf, 8) || !aligned(out, 2) ||
+        !aligned(a_gs, 4) || !aligned(b_alpha, 4))
+        return NVFP4_EINVAL;
+    int dv = check_device();
+    if (dv) return dv;
+    GemmParams p = {};
+    p.mode = kGemmDense;
+    p.aq = aq;
+    p.asf = asf;
+    p.M = M;
+    p.bq = bq;
+    p.bsf = bsf;
+    p.N = N;
+    p.K = K;
+    p.a_gs = a_gs;
+    p.b_alpha = b_alpha;
+    p.out_bf16 = out;
+    return hip_status(launch_gemm(p, stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
+    if (!moe_shape_ok(T, H, I, E, topk)) return 0;
+    return moe_layout(T, H, I, E, topk).total;
+}
+
+int nvfp4_moe_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                               size_t* offsets) {
+    if (!offsets) return NVFP4_EINVAL;
+    if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
+    const MoeLayout L = moe_layout(T, H, I, E, topk);
+    for (int i = 0; i < NVFP4_MOE_WS_NUM; ++i) offsets[i] = L.off[i];
+    return NVFP4_OK;
+}
+
+int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                      const uint8_t* w13, const uint8_t* w13_sf, const float* w13_alpha,
+                      const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha, int64_t T,
+                      int64_t H, int64_t I, int64_t E, int64_t topk, uint16_t* y, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return NVFP4_EINVAL;
+    if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
+    if (!w13 || !w13_sf || !w13_alpha || !w2 || !w2_sf || !w2_alpha) return NVFP4_EINVAL;
+    if (T > 0 && (!x || !topk_ids || !topk_weights || !y)) return NVFP4_EINVAL;
+    if (T > 0 && (!aligned(x, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) ||
+                  !aligned(topk_weights, 4)))
+        return NVFP4_EINVAL;
+    if (!aligned(w13, 4) || !aligned(w2, 4) || !aligned(w13_sf, 8) || !aligned(w2_sf, 8) ||
+        !aligned(w13_alpha, 4) || !aligned(w2_alpha, 4))
+        return NVFP4_EINVAL;
+    const MoeLayout L = moe_layout(T, H, I, E, topk);
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total)
+        return NVFP4_EWORKSPACE;
+    int dv = check_device();
+    if (dv) return dv;
+    if (T == 0) return NVFP4_OK;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* xq = ws + L.off[NVFP4_MOE_WS_XQ];
+    uint8_t* xsf = ws + L.off[NVFP4_MOE_WS_XSF];
+    float* gs1 = reinterpret_cast<float*>(ws + L.off[NVFP4_MOE_WS_GS1]);
+    float* gs2 = reinterpret_cast<float*>(ws + L.off[NVFP4_MOE_WS_GS2]);
+    int32_t* counts = reinterpret_cast<int32_t*>(ws + L.off[NVFP4_MOE_WS_COUNTS]);
+    int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.off[NVFP4_MOE_WS_OFFSETS]);
+    int32_t* sorted_slot = reinterpret_cast<int32_t*>(ws + L.off[NVFP4_MOE_WS_SORTED_SLOT]);
+    int32_t* slot_row = reinterpret_cast<int32_t*>(ws + L.off[NVFP4_MOE_WS_SLOT_ROW]);
+    uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.off[NVFP4_MOE_WS_ACT]);
+    uint8_t* aq = ws + L.off[NVFP4_MOE_WS_AQ];
+    uint8_t* asf = ws + L.off[NVFP4_MOE_WS_ASF];
+    float* o2 = reinterpret_cast<float*>(ws + L.off[NVFP4_MOE_WS_O2]);
+    uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
+    Tile* tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+    int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+    const int64_t S = T * topk;
+
+    auto mark = [&](int i) -> hipError_t {
+        return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
+    };
+
+    // 1. routing tables + tile list (also zeroes both amax slots)
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_ROUTE));
+    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, kGemmBM, counts, offsets, sorted_slot,
+                           slot_row, tiles, num_tiles, amax, 2, stream));
+    // 2. quantize x
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
+    NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
+    NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, xsf, gs1, stream));
+    // 3. L1 grouped GEMM with fused SiLU(gate) * up
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
+    GemmParams p1 = {};
+    p1.mode = kGemmL1;
+    p1.aq = xq;
+    p1.asf = xsf;
+    p1.a_gather = sorted_slot;
+    p1.topk = (int)topk;
+    p1.bq = w13;
+    p1.bsf = w13_sf;
+    p1.N = 2 * I;
+    p1.K = H;
+    p1.a_gs = gs1;
+    p1.b_alpha = w13_alpha;
+    p1.tiles = tiles;
+    p1.num_tiles = num_tiles;
+    p1.max_tiles = L.max_tiles;
+    p1.out_bf16 = act;
+    p1.I = I;
+    p1.amax_slot = amax + 1;
+    NVFP4_TRY(launch_gemm(p1, stream));
+    // 4. requantize act (rows of valid slots only: offsets[E])
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_REQUANT));
+    NVFP4_TRY(launch_quant_rows(act, S, I, offsets + E, amax + 1, aq, asf, gs2, stream));
+    // 5a. L2 grouped GEMM
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_L2));
+    GemmParams p2 = {};
+    p2.mode = kGemmL2;
+    p2.aq = aq;
+    p2.asf = asf;
+    p2.bq = w2;
+    p2.bsf = w2_sf;
+    p2.N = H;
+    p2.K = I;
+    p2.a_gs = gs2;
+    p2.b_alpha = w2_alpha;
+    p2.tiles = tiles;
+    p2.num_tiles = num_tiles;
+    p2.max_tiles = L.max_tiles;
+    p2.out_f32 = o2;
+    NVFP4_TRY(launch_gemm(p2, stream));
+    // 5b. weighted combine
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_COMBINE));
+    NVFP4_TRY(launch_combine(o2, slot_row, topk_weights, T, (int)topk, H, y, stream));
+    NVFP4_TRY(mark(NVFP4_MOE_NUM_STAGES));
+    return NVFP4_OK;
+}
+
+}  // extern "C"

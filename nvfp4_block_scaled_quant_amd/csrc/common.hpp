@@ -1,0 +1,172 @@
+// Device-side building blocks shared by the NVFP4 kernels (gfx950 only).
+//
+// Number formats follow the "nvfp4-megamoe-kernel" pages: E2M1 nibbles are
+// sign-magnitude (bit 3 sign, bits 2:0 index {0,.5,1,1.5,2,3,4,6}), two per
+// byte with the even element low; scale bytes are OCP E4M3FN bit patterns
+// (bias 7, max 448) per 16 elements (DEBUG_LOG Hypothesis 5/6, src commit log
+// quantizer and `.view` fixes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kSixTimesE4M3Max = 2688.0f;   // 6 * 448, exact
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 quantization arithmetic. Every operation is one IEEE float32 operation
+// with round-to-nearest-even; divisions are the correctly rounded ones (the
+// library is built with -fhip-fp32-correctly-rounded-divide-sqrt and
+// -ffp-contract=off).
+// ---------------------------------------------------------------------------
+struct QuantScales {
+    float gs;       // amax / 2688
+    float six_gs;   // 6 * gs
+};
+
+__device__ __forceinline__ QuantScales make_scales(float amax) {
+    QuantScales s;
+    s.gs = amax / kSixTimesE4M3Max;
+    s.six_gs = 6.0f * s.gs;
+    return s;
+}
+
+// E4M3FN code nearest to s in [0, 448], ties to the even code.
+// Subnormal range (s < 2^-6): spacing 2^-9, code = rint(s * 2^9).
+// Normal range: with e = floor(log2 s) in [-6, 8], r = rint(s * 2^(3-e)) in
+// [8, 16] and code = (e + 6) * 8 + r; r = 16 carries into the next binade.
+__device__ __forceinline__ uint32_t e4m3_encode(float s) {
+    if (s < 0.015625f) {
+        return (uint32_t)__builtin_rintf(s * 512.0f);
+    }
+    const int e = (int)((__float_as_uint(s) >> 23) & 0xFF) - 127;
+    const float scaled = s * __uint_as_float((uint32_t)(127 + 3 - e) << 23);
+    const uint32_t r = (uint32_t)__builtin_rintf(scaled);
+    return (uint32_t)((e + 6) << 3) + r;
+}
+
+// E4M3FN code (0x00..0x7E) -> float32 value, exact.
+__device__ __forceinline__ float e4m3_decode(uint32_t code) {
+    return __builtin_amdgcn_cvt_f32_fp8(code, 0);
+}
+
+// E2M1 magnitude index of v >= 0: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
+// even index, saturating above 6. The midpoints 0.25, 0.75, ..., 5 belong to
+// the even neighbour, hence the alternating strict / non-strict comparisons.
+__device__ __forceinline__ uint32_t e2m1_magnitude(float v) {
+    return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+           (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+           (uint32_t)(v > 5.0f);
+}
+
+// Quantize one 16-element block given as 16 bf16 bit patterns in 8 words
+// (element 2i in the low half of word i). Writes 8 packed bytes (2 words) and
+// returns the scale byte.
+__device__ __forceinline__ uint32_t quantize_block16(const uint32_t (&w)[8], const QuantScales& qs,
+                                                     uint32_t (&packed)[2]) {
+    uint32_t bmax_bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+        bmax_bits = max(bmax_bits, max(lo, hi));
+    }
+    const float bmax = bf16_to_f32(bmax_bits);
+    float s = 0.0f;
+    if (qs.gs > 0.0f) {
+        s = bmax / qs.six_gs;
+        s = fminf(s, 448.0f);
+    }
+    const uint32_t code = e4m3_encode(s);
+    const float den = e4m3_decode(code) * qs.gs;
+    uint32_t nib[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
+            uint32_t mag = 0;
+            if (den > 0.0f) {
+                const float v = bf16_to_f32(b & 0x7FFFu) / den;
+                mag = e2m1_magnitude(v);
+            }
+            nib[2 * i + h] = ((b >> 12) & 8u) | mag;
+        }
+    }
+    packed[0] = 0;
+    packed[1] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[0] |= nib[i] << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[1] |= nib[8 + i] << (4 * i);
+    return code;
+}
+
+// ---------------------------------------------------------------------------
+// Dequantization for the MFMA operands.
+// The FP4 -> f16 conversion applies only the exponent of its float scale, so
+// it is given 2^8, and the E4M3 scale enters as an f16 multiply: shifting an
+// E4M3 byte left by 7 gives the f16 bit pattern of e4m3 * 2^-8 (bias 7 vs 15,
+// the subnormal ranges line up). Every product e2m1 * e4m3 has at most 6
+// significant bits and lies in [2^-10, 2688], so it is exact in f16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ half2_t scale_pair(uint32_t code) {
+    const uint32_t b = code << 7;
+    return __builtin_bit_cast(half2_t, b | (b << 16));
+}
+
+// 8 nibbles of `word` (element i in bits 4i..4i+3) -> 8 f16 values * scale.
+__device__ __forceinline__ half8_t dequant8(uint32_t word, half2_t sp) {
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 0) * sp;
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 1) * sp;
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 2) * sp;
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 3) * sp;
+    half8_t r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// Byte transpose of a 4x4 block held in 4 words: in r[i] byte j = M[i][j];
+// out c[j] byte i = M[i][j].
+__device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&c)[4]) {
+    const uint32_t t01lo = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+    const uint32_t t01hi = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+    const uint32_t t23lo = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const uint32_t t23hi = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    c[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
+    c[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+    c[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+    c[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
+}
+
+}  // namespace nvfp4

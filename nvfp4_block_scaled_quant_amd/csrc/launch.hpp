@@ -1,0 +1,87 @@
+// Host-side launchers of the NVFP4 kernels. Each returns hipSuccess or the
+// launch error; none synchronizes and none allocates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Tile descriptor of the grouped GEMMs: rows [row_start, row_start + row_count)
+// of the sorted slot order, all routed to `expert`.
+struct Tile {
+    int32_t expert;
+    int32_t row_start;
+    int32_t row_count;
+    int32_t pad;
+};
+
+constexpr int kGemmBM = 256;      // rows per GEMM tile
+constexpr int kGemmBN = 256;      // B columns per GEMM tile (L1: 128 gate + 128 up)
+constexpr int kRouteThreads = 1024;
+constexpr int kMaxExperts = 512;
+
+// zero `n` 32-bit words
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
+// amax over `n` bf16 values (n % 8 == 0, 16-byte aligned) into *slot as float
+// bits (atomic max; *slot must hold 0 or a smaller value).
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* slot, hipStream_t s);
+
+// Per-matrix amax of E matrices of `per` bf16 values each into slots[e].
+hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, uint32_t* slots,
+                                    hipStream_t s);
+
+// Row-block quantization of x (M, K) with amax taken from *amax_slot. Rows at or
+// beyond *m_dev (when m_dev is not null) are left untouched. gs_out receives gs.
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
+                             const uint32_t* amax_slot, uint8_t* q, uint8_t* sf, float* gs_out,
+                             hipStream_t s);
+
+// Column-block quantization of E weight matrices (E, K, N) with per-matrix amax.
+hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
+                             const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
+                             hipStream_t s);
+
+// Routing tables and the tile list (single work-group kernel). Also zeroes
+// `zero_slots` (n_zero words) before anything else in the layer runs.
+hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                        int32_t* slot_row, Tile* tiles, int32_t* num_tiles,
+                        uint32_t* zero_slots, int n_zero, hipStream_t s);
+
+// y[t] = bf16(sum_j w[t][j] * o2[slot_row[t*topk+j]]) for rows that exist.
+hipError_t launch_combine(const float* o2, const int32_t* slot_row, const float* weights,
+                          int64_t T, int topk, int64_t H, uint16_t* y, hipStream_t s);
+
+enum GemmMode { kGemmDense = 0, kGemmL1 = 1, kGemmL2 = 2 };
+
+struct GemmParams {
+    int mode;
+    // A: rows of quantized activations
+    const uint8_t* aq;
+    const uint8_t* asf;
+    int64_t M;                 // dense: rows of A
+    const int32_t* a_gather;   // L1: sorted row -> slot index; token = slot / topk
+    int topk;
+    // B: per-expert K-packed weights
+    const uint8_t* bq;
+    const uint8_t* bsf;
+    int64_t N;                 // columns of B
+    int64_t K;
+    const float* a_gs;         // device scalar
+    const float* b_alpha;      // device, one per expert
+    // grouped tiles
+    const Tile* tiles;
+    const int32_t* num_tiles;
+    int64_t max_tiles;
+    // outputs
+    uint16_t* out_bf16;        // dense: (M, N); L1: act (S, I)
+    float* out_f32;            // L2: (S, N)
+    int64_t I;                 // L1: act columns (N = 2I)
+    uint32_t* amax_slot;       // L1: act amax (atomic max of float bits)
+};
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+}  // namespace nvfp4

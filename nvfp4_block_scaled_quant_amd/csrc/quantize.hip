@@ -1,0 +1,166 @@
+// NVFP4 dynamic quantization kernels (gfx950).
+//
+// The rule is the pages' stage_activation / weight-loader rule (DEBUG_LOG,
+// Hypothesis 6 steps 1-5; "NVFP4 MoE Pipeline"): global scale amax/(6*448) over
+// the whole tensor, E4M3 block scale block_amax/(6*global) per 16 elements,
+// nearest E2M1, even element in the low nibble. The arithmetic order is fixed
+// in common.hpp (quantize_block16) and is float32 IEEE throughout.
+//
+// Two passes: an amax pass (integer max of bf16 magnitude bits, which orders
+// like the values; one atomic max per work-group) and a quantize pass in which
+// every thread owns one 16-element block. Both are HBM-bound streaming kernels:
+// 16-byte loads, consecutive threads on consecutive addresses.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+__device__ __forceinline__ void block_atomic_max(uint32_t v, uint32_t* slot) {
+    __shared__ uint32_t red[kThreads / 64];
+    v = wave_max_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = red[0];
+        for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+        // bf16 magnitude bits -> float bits of the same value
+        atomicMax(slot, m << 16);
+    }
+}
+
+// x: n bf16 values, n % 8 == 0, 16-byte aligned. Segment `blockIdx.y` of
+// length `per` (batched variant) or the whole array (gridDim.y == 1).
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ x, int64_t per,
+                                                        uint32_t* __restrict__ slots) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)blockIdx.y * per);
+    const int64_t nvec = per / 8;
+    uint32_t m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * kThreads) {
+        const u32x4 v = p[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            m = max(m, v[c] & 0x7FFFu);
+            m = max(m, (v[c] >> 16) & 0x7FFFu);
+        }
+    }
+    block_atomic_max(m, slots + blockIdx.y);
+}
+
+// One thread per 16-element block of a row-major (M, K) bf16 matrix.
+__global__ __launch_bounds__(kThreads) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ m_dev,
+    const uint32_t* __restrict__ amax_slot, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+    float* __restrict__ gs_out) {
+    const float amax = __uint_as_float(*amax_slot);
+    const QuantScales qs = make_scales(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = qs.gs;
+    const int64_t rows = m_dev ? min((int64_t)(*m_dev), M) : M;
+    const int64_t groups = K / 16;
+    const int64_t nblocks = rows * groups;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
+         b += (int64_t)gridDim.x * kThreads) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
+        const u32x4 v0 = src[0];
+        const u32x4 v1 = src[1];
+        const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t packed[2];
+        const uint32_t code = quantize_block16(w, qs, packed);
+        u32x2 out;
+        out[0] = packed[0];
+        out[1] = packed[1];
+        *reinterpret_cast<u32x2*>(q + b * 8) = out;
+        sf[b] = (uint8_t)code;
+    }
+}
+
+// One thread per (matrix e, K-group g, column n) of E row-major (K, N) bf16
+// matrices; blocks run along K. Output byte [e][8g + j][n] holds the nibbles
+// of k = 16g + 2j (low) and 16g + 2j + 1 (high).
+__global__ __launch_bounds__(kThreads) void quant_cols_kernel(
+    const uint16_t* __restrict__ w, int64_t K, int64_t N, const uint32_t* __restrict__ amax_slots,
+    uint8_t* __restrict__ q, uint8_t* __restrict__ sf, float* __restrict__ alpha) {
+    const int64_t e = blockIdx.y;
+    const QuantScales qs = make_scales(__uint_as_float(amax_slots[e]));
+    const int64_t groups = K / 16;
+    const int64_t per = groups * N;
+    const uint16_t* we = w + e * K * N;
+    if (blockIdx.x == 0 && threadIdx.x == 0) alpha[e] = qs.gs;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < per;
+         i += (int64_t)gridDim.x * kThreads) {
+        const int64_t g = i / N, n = i - g * N;
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = we[(16 * g + 2 * j) * N + n];
+            const uint32_t hi = we[(16 * g + 2 * j + 1) * N + n];
+            v[j] = lo | (hi << 16);
+        }
+        uint32_t packed[2];
+        const uint32_t code = quantize_block16(v, qs, packed);
+        uint8_t* qe = q + e * (K / 2) * N;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t word = packed[j >> 2];
+            qe[(8 * g + j) * N + n] = (uint8_t)(word >> (8 * (j & 3)));
+        }
+        sf[e * per + g * N + n] = (uint8_t)code;
+    }
+}
+
+int grid_for(int64_t work, int64_t cap) {
+    int64_t g = (work + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s) {
+    zero_u32_kernel<<<1, 64, 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* slot, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int g = grid_for(n / 8, 2048);
+    amax_kernel<<<dim3(g, 1), kThreads, 0, s>>>(x, n, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, uint32_t* slots,
+                                    hipStream_t s) {
+    if (E <= 0 || per <= 0) return hipSuccess;
+    const int g = grid_for(per / 8, 512);
+    amax_kernel<<<dim3(g, (unsigned)E), kThreads, 0, s>>>(x, per, slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
+                             const uint32_t* amax_slot, uint8_t* q, uint8_t* sf, float* gs_out,
+                             hipStream_t s) {
+    const int g = grid_for(M * (K / 16), 1 << 20);
+    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, q, sf, gs_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
+                             const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
+                             hipStream_t s) {
+    if (E <= 0) return hipSuccess;
+    const int g = grid_for((K / 16) * N, 4096);
+    quant_cols_kernel<<<dim3(g, (unsigned)E), kThreads, 0, s>>>(w, K, N, amax_slots, q, sf, alpha);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,171 @@
+// Token-to-expert permutation and the routing-weighted combine (gfx950).
+//
+// The pages name the permutation ("slots", "slot_token") and the final
+// "scatter with routing weights" (DEBUG_LOG, "Pipeline Trace" and "NVFP4 MoE
+// Pipeline") without defining them. The reading implemented here: one slot per
+// (token t, choice j), s = t * topk + j, whose expert id is in [0, E); slots
+// are sorted by expert, stably by slot index, so every expert's rows form one
+// contiguous range of the "sorted row" order the grouped GEMMs walk; slots with
+// other ids are skipped. The combine is y[t] = sum over j, in j order, of
+// topk_weights[t][j] times the L2 row of slot (t, j), float32, then one bf16
+// rounding.
+//
+// Routing runs in a single 1024-thread work-group: it is a few microseconds of
+// integer work on at most a few tens of thousands of slots and it produces the
+// whole tile list on the device, so the host never waits for counts.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+
+namespace {
+
+constexpr int kWaves = kRouteThreads / 64;
+
+// Dynamic LDS: cnt[E], off[E+1], run[E], wcnt[kWaves][E]
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const int32_t* __restrict__ ids, int64_t S, int E, int BM, int nbits,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ slot_row, Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles,
+    uint32_t* __restrict__ zero_slots, int n_zero) {
+    extern __shared__ int32_t lds[];
+    int32_t* cnt = lds;
+    int32_t* off = cnt + E;
+    int32_t* run = off + E + 1;
+    int32_t* wcnt = run + E;
+    __shared__ int32_t tile_base[kMaxExperts + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < n_zero; i += kRouteThreads) zero_slots[i] = 0u;
+    for (int e = tid; e < E; e += kRouteThreads) { cnt[e] = 0; run[e] = 0; }
+    __syncthreads();
+
+    // histogram
+    for (int64_t s = tid; s < S; s += kRouteThreads) {
+        const int e = ids[s];
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+
+    // exclusive scans of counts and of tiles per expert
+    if (tid == 0) {
+        int acc = 0, tacc = 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = acc;
+            tile_base[e] = tacc;
+            acc += cnt[e];
+            tacc += (cnt[e] + BM - 1) / BM;
+        }
+        off[E] = acc;
+        tile_base[E] = tacc;
+        *num_tiles = tacc;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
+    for (int e = tid; e < E; e += kRouteThreads) {
+        counts[e] = cnt[e];
+        const int nt = (cnt[e] + BM - 1) / BM;
+        for (int i = 0; i < nt; ++i) {
+            Tile t;
+            t.expert = e;
+            t.row_start = off[e] + i * BM;
+            t.row_count = min(BM, cnt[e] - i * BM);
+            t.pad = 0;
+            tiles[tile_base[e] + i] = t;
+        }
+    }
+
+    // stable scatter: chunks of kRouteThreads slots in order; inside a chunk a
+    // slot's rank is (same-expert slots of earlier waves) + (same-expert lanes
+    // below it in its own wave, found by matching the id bit by bit)
+    for (int64_t c0 = 0; c0 < S; c0 += kRouteThreads) {
+        for (int i = tid; i < kWaves * E; i += kRouteThreads) wcnt[i] = 0;
+        __syncthreads();
+        const int64_t s = c0 + tid;
+        const int e = (s < S) ? ids[s] : -1;
+        const bool valid = (e >= 0 && e < E);
+        uint64_t match = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = valid && ((e >> b) & 1);
+            const uint64_t bl = __ballot(bit);
+            match &= bit ? bl : ~bl;
+        }
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank = __popcll(match & below);
+        const int total = __popcll(match);
+        if (valid && rank == total - 1) wcnt[wave * E + e] = total;
+        __syncthreads();
+        if (valid) {
+            int base = run[e];
+            for (int w = 0; w < wave; ++w) base += wcnt[w * E + e];
+            const int pos = off[e] + base + rank;
+            sorted_slot[pos] = (int32_t)s;
+            slot_row[s] = pos;
+        } else if (s < S) {
+            slot_row[s] = -1;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kRouteThreads) {
+            int add = 0;
+            for (int w = 0; w < kWaves; ++w) add += wcnt[w * E + ee];
+            run[ee] += add;
+        }
+        __syncthreads();
+    }
+}
+
+// One thread per 8 consecutive columns of one token; `chunks` work-groups of
+// 256 threads per token.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o2,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ weights, int topk,
+                                                      int64_t H, int chunks, uint16_t* __restrict__ y) {
+    const int64_t t = blockIdx.x / chunks;
+    const int64_t c0 = ((int64_t)(blockIdx.x % chunks) * 256 + threadIdx.x) * 8;
+    if (c0 >= H) return;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+        const int32_t row = slot_row[t * topk + j];
+        if (row < 0) continue;
+        const float w = weights[t * topk + j];
+        const float4_t* src = reinterpret_cast<const float4_t*>(o2 + (int64_t)row * H + c0);
+        const float4_t a = src[0], b = src[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] = acc[i] + w * a[i];
+            acc[4 + i] = acc[4 + i] + w * b[i];
+        }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        out[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x4*>(y + t * H + c0) = out;
+}
+
+}  // namespace
+
+hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
+                        int32_t* num_tiles, uint32_t* zero_slots, int n_zero, hipStream_t s) {
+    (void)topk;
+    int nbits = 1;
+    while ((1 << nbits) < E) ++nbits;
+    const size_t lds = sizeof(int32_t) * ((size_t)E * (3 + kWaves) + 1);
+    route_kernel<<<1, kRouteThreads, lds, s>>>(ids, S, E, BM, nbits, counts, offsets, sorted_slot,
+                                               slot_row, tiles, num_tiles, zero_slots, n_zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o2, const int32_t* slot_row, const float* weights,
+                          int64_t T, int topk, int64_t H, uint16_t* y, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    const int chunks = (int)((H / 8 + 255) / 256);
+    combine_kernel<<<(unsigned)(T * chunks), 256, 0, s>>>(o2, slot_row, weights, topk, H, chunks, y);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

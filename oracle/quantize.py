@@ -50,16 +50,28 @@ def quantize_f32(x):
     """Quantize a float32 matrix (rows, cols), blocks of 16 along cols.
 
     Returns (q uint8 (rows, cols/2), sf uint8 (rows, cols/16), gs float32).
+    The global scale needs the whole tensor's amax first; after that every
+    row is independent, so rows are processed in chunks to bound memory.
     """
     x = np.asarray(x, dtype=F32)
     if x.ndim != 2 or x.shape[1] % BLOCK:
         raise ValueError("quantize expects a 2-D array with cols % 16 == 0")
     rows, cols = x.shape
-    ax = np.abs(x)
-    amax = F32(ax.max()) if x.size else F32(0.0)
+    amax = F32(np.abs(x).max()) if x.size else F32(0.0)
     gs = global_scale(amax)
-    six_gs = F32(F32(6.0) * gs)
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    sf = np.empty((rows, cols // BLOCK), dtype=np.uint8)
+    step = max(1, (1 << 18) // max(cols, 1))
+    for r0 in range(0, rows, step):
+        q[r0:r0 + step], sf[r0:r0 + step] = _quantize_rows(x[r0:r0 + step], gs)
+    return q, sf, gs
 
+
+def _quantize_rows(x, gs):
+    """Steps 2-4 of the rule for some rows, given the tensor's global scale."""
+    rows, cols = x.shape
+    ax = np.abs(x)
+    six_gs = F32(F32(6.0) * gs)
     bmax = ax.reshape(rows, cols // BLOCK, BLOCK).max(axis=2)
     if gs > 0:
         s = (bmax / six_gs).astype(F32)
@@ -77,7 +89,7 @@ def quantize_f32(x):
     mag = e2m1_encode_magnitude(v)
     nib = (np.signbit(x).astype(np.uint8) << 3) | mag
     q = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
-    return q, sf.astype(np.uint8), gs
+    return q, sf.astype(np.uint8)
 
 
 def quantize_bf16(x_bits):

@@ -24,3 +24,37 @@ def read_golden(name):
             if line:
                 rows.append(line.split())
     return rows
+
+
+@pytest.fixture(scope="session")
+def nv():
+    """The HIP library binding on cuda:0 (fails loudly when either is missing)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    import nvfp4_block_scaled_quant_amd as nv
+    return nv
+
+
+def to_dev(a, dtype=None):
+    """NumPy array -> cuda tensor with the same bits (uint16 -> bf16 view)."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def to_host(t):
+    """cuda tensor -> NumPy array with the same bits (bf16 -> uint16)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects
+bad arguments on the host before touching any device (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import nvfp4_block_scaled_quant_amd as nv
+    return nv
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("nvfp4_quantize", "nvfp4_moe_forward", "nvfp4_gemm", "nvfp4_strerror",
+                 "nvfp4_quantize_weights", "nvfp4_moe_workspace"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(nv):
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in nvfp4moe.h but not exported"
+    assert set(declared_functions()) == set(nv.EXPORTED)
+
+
+def test_strerror_and_version(nv):
+    assert nv.version() == (1, 0)
+    for code in range(6):
+        assert len(nv.strerror(code)) > 0
+    assert nv.strerror(99) == "unknown status"
+
+
+L = None
+
+
+def lib(nv):
+    return nv._lib
+
+
+def p(v):
+    return ctypes.c_void_p(v)
+
+
+A16 = 1 << 20          # a fake, aligned, never-dereferenced address
+
+
+def test_quantize_argument_errors(nv):
+    f = lib(nv).nvfp4_quantize
+    ws = p(A16)
+    assert f(p(A16), 4, 15, p(A16), p(A16), p(A16), ws, 256, None) == 2     # K % 16
+    assert f(p(A16), -1, 16, p(A16), p(A16), p(A16), ws, 256, None) == 1    # M < 0
+    assert f(p(A16), 4, 16, p(A16), p(A16), p(0), ws, 256, None) == 1       # gs null
+    assert f(p(0), 4, 16, p(A16), p(A16), p(A16), ws, 256, None) == 1       # x null
+    assert f(p(A16 + 2), 4, 16, p(A16), p(A16), p(A16), ws, 256, None) == 1  # x misaligned
+    assert f(p(A16), 4, 16, p(A16), p(A16), p(A16), ws, 8, None) == 3       # ws small
+    assert f(p(A16), 4, 16, p(A16), p(A16), p(A16), p(A16 + 8), 256, None) == 3  # ws align
+    assert lib(nv).nvfp4_quantize_workspace(4, 16) >= 4
+
+
+def test_quantize_weights_argument_errors(nv):
+    f = lib(nv).nvfp4_quantize_weights
+    assert f(p(A16), 2, 24, 16, p(A16), p(A16), p(A16), p(A16), 256, None) == 2
+    assert f(p(A16), -2, 32, 16, p(A16), p(A16), p(A16), p(A16), 256, None) == 1
+    assert f(p(0), 2, 32, 16, p(A16), p(A16), p(A16), p(A16), 256, None) == 1
+    assert f(p(A16), 2, 32, 16, p(A16), p(A16), p(A16), p(A16), 4, None) == 3
+    assert f(p(0), 0, 32, 16, p(0), p(0), p(0), p(0), 0, None) == 0          # E == 0: nothing
+
+
+def test_gemm_argument_errors(nv):
+    f = lib(nv).nvfp4_gemm
+    args = [p(A16)] * 6
+    assert f(*args, 4, 16, 24, p(A16), None) == 2       # K % 16
+    assert f(*args, 4, 24, 32, p(A16), None) == 2       # N % 16
+    assert f(*args, -4, 16, 32, p(A16), None) == 1
+    assert f(*args, 0, 16, 32, p(A16), None) == 0       # M == 0: nothing to do
+    bad = [p(A16)] * 5 + [p(0)]
+    assert f(*bad, 4, 16, 32, p(A16), None) == 1
+
+
+def test_moe_argument_errors(nv):
+    f = lib(nv).nvfp4_moe_forward
+    ptrs9 = [p(A16)] * 9
+
+    def call(T, H, I, E, k, ws_bytes=1 << 40, ws=A16, ptrs=ptrs9, y=A16):
+        return f(*ptrs, T, H, I, E, k, p(y), p(ws), ws_bytes, None, None)
+
+    assert call(8, 7168, 3072, 48, 49) == 2          # topk > E
+    assert call(8, 7000, 3072, 48, 8) == 2           # H % 16
+    assert call(8, 7168, 3000, 48, 8) == 2           # I % 16
+    assert call(8, 7168, 3072, 513, 8) == 2          # E above the supported maximum
+    assert call(-1, 7168, 3072, 48, 8) == 1
+    assert call(8, 7168, 3072, 48, 0) == 1
+    assert call(8, 7168, 3072, 48, 8, ws_bytes=1024) == 3
+    assert call(8, 7168, 3072, 48, 8, ws=A16 + 64) == 3
+    assert call(8, 7168, 3072, 48, 8, ptrs=[p(A16 + 4)] + ptrs9[1:]) == 1   # x misaligned
+    assert call(8, 7168, 3072, 48, 8, ptrs=ptrs9[:3] + [p(0)] + ptrs9[4:]) == 1
+    assert call(8, 7168, 3072, 48, 8, y=0) == 1
+
+
+def test_moe_workspace_layout_is_consistent(nv):
+    for shape in [(32, 256, 128, 4, 2), (8, 7168, 3072, 48, 8), (4096, 7168, 3072, 48, 8),
+                  (1, 16, 16, 1, 1), (0, 16, 16, 1, 1)]:
+        T, H, I, E, k = shape
+        total = nv.moe_workspace_size(*shape)
+        lay = nv.moe_workspace_layout(*shape)
+        S = T * k
+        ends = {"xq": T * H // 2, "xsf": T * H // 16, "gs1": 4, "gs2": 4, "counts": 4 * E,
+                "offsets": 4 * (E + 1), "sorted_slot": 4 * S, "slot_row": 4 * S,
+                "act": 2 * S * I, "aq": S * I // 2, "asf": S * I // 16, "o2": 4 * S * H}
+        spans = sorted((lay[n], lay[n] + ends[n]) for n in ends)
+        for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+            assert a1 <= b0
+        assert all(lay[n] % 256 == 0 for n in lay)
+        assert spans[-1][1] <= total
+    with pytest.raises(Exception):
+        nv.moe_workspace_size(8, 7168, 3072, 48, 49)
+
+
+def test_binding_requires_device_tensors(nv):
+    import torch
+    with pytest.raises(TypeError):
+        nv.quantize(torch.zeros((4, 16), dtype=torch.bfloat16))
