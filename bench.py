@@ -1,0 +1,268 @@
+"""Benchmark of the NVFP4 expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one nvfp4_moe_forward (quantize x, route, L1 grouped GEMM with fused
+SiLU*up, requantize, L2 grouped GEMM, weighted combine) over the prefill batch:
+4096 tokens, hidden 7168, intermediate 3072, 48 local experts, top-8, x bf16
+N(0,1)*3 with 0.1% outliers at +-40, router logits N(0,1), softmax-renormalized
+top-8 weights, weights bf16 N(0, 0.02) quantized with the NVFP4 weight rule by
+the library's own nvfp4_quantize_weights. Inputs are synthetic and resident in
+HBM before the timed region starts.
+
+The JSON line reports tokens/s (value), effective TFLOP/s (6 * slots * H * I per
+step), per-stage device times from HIP events recorded by the library on its
+stream, the L1 GEMM's MFMA roofline fraction, a decode-batch measurement (8
+tokens, weight HBM GB/s) and the CPU oracle timed on a bounded sample of the
+prefill workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_MFMA_TFLOPS = 2500.0     # MI355X dense f16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "l1_gemm_prefill_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
+    return ap.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp", "launch.hpp"):
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def make_weights(nv, cfg):
+    """Per-expert bf16 weights from the workload recipe, quantized on the GPU."""
+    import torch
+    import workloads as W
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w13q = torch.empty((E, H // 2, 2 * I), dtype=torch.uint8, device="cuda")
+    w13sf = torch.empty((E, H // 16, 2 * I), dtype=torch.uint8, device="cuda")
+    w2q = torch.empty((E, I // 2, H), dtype=torch.uint8, device="cuda")
+    w2sf = torch.empty((E, I // 16, H), dtype=torch.uint8, device="cuda")
+    w13a = torch.empty((E,), dtype=torch.float32, device="cuda")
+    w2a = torch.empty((E,), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        w13, w2 = W.expert_weights_bf16(cfg, e)
+        q, sf, a = nv.quantize_weights(to_dev(w13)[None])
+        w13q[e], w13sf[e], w13a[e] = q[0], sf[0], a[0]
+        q, sf, a = nv.quantize_weights(to_dev(w2)[None])
+        w2q[e], w2sf[e], w2a[e] = q[0], sf[0], a[0]
+    if cfg.alpha_loguniform:
+        a13, a2 = W.alphas_loguniform(cfg)
+        w13a.copy_(torch.from_numpy(a13))
+        w2a.copy_(torch.from_numpy(a2))
+    torch.cuda.synchronize()
+    return w13q, w13sf, w13a, w2q, w2sf, w2a
+
+
+def time_layer(nv, cfg, weights, steps, warmup):
+    """Run warmup + timed steps; return (ms per step, per-stage ms, S_valid)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    x = to_dev(W.activations(cfg))
+    ids_np, wts_np = W.routing(cfg)
+    ids, wts = to_dev(ids_np), to_dev(wts_np)
+    s_valid = int(((ids_np >= 0) & (ids_np < cfg.E)).sum())
+    ws = torch.empty((nv.moe_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk),),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+
+    def step(ev=None):
+        nv.moe_forward(x, ids, wts, *weights, y=y, workspace=ws, stage_events=ev)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [nv.StageEvents() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = [ev.elapsed_ms() for ev in events]
+    stage_ms = {k: float(np.mean([p[k] for p in per])) for k in per[0]}
+    ok = bool(torch.isfinite(y.float()).all().item())
+    return (t1 - t0) * 1e3 / steps, stage_ms, s_valid, ids_np, ok
+
+
+def decode_bytes(cfg, ids_np):
+    """Algorithmic HBM bytes of one decode step: every touched expert's w13 and
+    w2 bytes and scales, plus x, y, the routing arrays and the intermediates."""
+    import numpy as np
+    H, I, E = cfg.H, cfg.I, cfg.E
+    per_expert = (H // 2) * 2 * I + (H // 16) * 2 * I + (I // 2) * H + (I // 16) * H
+    touched = len(np.unique(ids_np[(ids_np >= 0) & (ids_np < E)]))
+    S = cfg.T * cfg.topk
+    act = S * I * 2 * 2 + S * (I // 2 + I // 16) * 2 + S * H * 4 * 2
+    return touched * per_expert + cfg.T * H * 2 * 2 + act, touched
+
+
+def cpu_baseline(cfg, experts=(0, 1)):
+    """The oracle's layer forward timed on a bounded sample of the prefill
+    workload: all T tokens' x, but only the slots routed to `experts` (the other
+    slots are skipped), with those experts' weights quantized by the oracle
+    (untimed). Reported as token-equivalents per second: sample slots / topk /
+    seconds."""
+    import numpy as np
+    import workloads as W
+    from oracle.moe import moe_forward
+    from oracle.quantize import quantize_weight_bf16
+    x = W.activations(cfg)
+    ids, wts = W.routing(cfg)
+    keep = np.isin(ids, experts)
+    ids_s = np.where(keep, ids, -1).astype(np.int32)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    w13q = np.zeros((E, H // 2, 2 * I), np.uint8)
+    w13sf = np.zeros((E, H // 16, 2 * I), np.uint8)
+    w2q = np.zeros((E, I // 2, H), np.uint8)
+    w2sf = np.zeros((E, I // 16, H), np.uint8)
+    w13a = np.zeros(E, np.float32)
+    w2a = np.zeros(E, np.float32)
+    for e in experts:
+        w13, w2 = W.expert_weights_bf16(cfg, e)
+        w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16(w13)
+        w2q[e], w2sf[e], w2a[e] = quantize_weight_bf16(w2)
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = None
+    t0 = time.perf_counter()
+    moe_forward(x, ids_s, wts, w13q, w13sf, w13a, w2q, w2sf, w2a)
+    dt = time.perf_counter() - t0
+    slots = int(keep.sum())
+    cores = len(os.sched_getaffinity(0))
+    return {"value": slots / cfg.topk / dt, "unit": "tokens/s", "cores": cores,
+            "blas_threads": blas_threads, "kind": "oracle", "seconds": dt,
+            "sample": (f"prefill workload (T={cfg.T}, H={H}, I={I}, E={E}, top-{cfg.topk}): all "
+                       f"tokens' x quantized, only the {slots} slots routed to experts "
+                       f"{list(experts)} run through L1/SiLU/requant/L2/combine; value = "
+                       f"slots/topk per second (token-equivalents); float64 BLAS matmuls "
+                       f"multithreaded, the rest single-threaded NumPy")}
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the layer is measured on one GPU's share of experts)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import nvfp4_block_scaled_quant_amd as nv
+    import workloads as W
+
+    cfg = W.PREFILL
+    t_setup = time.perf_counter()
+    weights = make_weights(nv, cfg)
+    setup_s = time.perf_counter() - t_setup
+    ms, stage_ms, s_valid, ids_np, finite = time_layer(nv, cfg, weights, args.steps, args.warmup)
+    flops = 6.0 * s_valid * cfg.H * cfg.I
+    l1_flops = 2.0 * s_valid * cfg.H * 2 * cfg.I
+    l1_tflops = l1_flops / (stage_ms["l1"] * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("gemm_source_hash") == gemm_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": "NVFP4 MoE layer tokens/s + eff. TFLOP/s (prefill); weight HBM GB/s (decode)",
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 x e4m3/16) operands, f16 MFMA, f32 accumulate, bf16 out",
+        "data": "synthetic",
+        "config": {"workload": "prefill", "tokens": cfg.T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "topk": cfg.topk,
+                   "slots": s_valid, "parallelism": "single GPU, one GPU's expert share"},
+        "eff_tflops": flops / (ms * 1e-3) / 1e12,
+        "stage_ms": stage_ms,
+        "roofline": {"bound": "mfma", "kernel": "L1 grouped GEMM (gemm_kernel<1>)",
+                     "achieved": l1_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": l1_tflops / PEAK_F16_MFMA_TFLOPS, "traffic": traffic,
+                     "algorithmic_flop_per_launch": l1_flops,
+                     "fp4_peak_frac": l1_tflops / 10100.0},
+        "finite": finite,
+        "setup_s": setup_s,
+        "note": "the source pages publish no throughput figures, only correctness traces on "
+                "their own (NVIDIA) hardware",
+    }
+    if not args.no_decode:
+        dcfg = W.DECODE
+        dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, args.decode_steps, 5)
+        nbytes, touched = decode_bytes(dcfg, dids)
+        out["decode"] = {"workload": "decode", "tokens": dcfg.T, "us_per_step": dms * 1e3,
+                         "touched_experts": touched, "algorithmic_bytes": nbytes,
+                         "GBps": nbytes / (dms * 1e-3) / 1e9,
+                         "hbm_frac": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "stage_us": {k: v * 1e3 for k, v in dstage.items()},
+                         "finite": dfin}
+    del weights
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,22 +9,24 @@
 // float32 alpha, in the epilogue. gfx950's FP4 MFMAs take power-of-two (E8M0)
 // scales per 32 elements and cannot carry an E4M3 scale per 16 elements
 // exactly, so the operands are dequantized in registers and fed to
-// v_mfma_f32_16x16x32_f16.
+// v_mfma_f32_32x32x16_f16.
 //
 // Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
-// 128 x 128 quadrant (8 x 8 MFMA tiles of 16 x 16). The K loop steps 128
+// 128 x 128 quadrant (4 x 4 tiles of v_mfma_f32_32x32x16_f16). The K loop steps 128
 // elements (64 packed bytes) at a time through double-buffered LDS holding the
 // tiles still packed (4 bits per element), so LDS traffic and capacity are a
 // quarter of a bf16 design. Both operands sit in LDS K-contiguous: A rows are
 // K-packed already; B arrives (K/2, N) N-contiguous from HBM and is transposed
 // 4x4 bytes at a time in registers (v_perm) on its way into LDS.
 //
-// K permutation. Inside one 128-element K step, lane group q = lane / 16 reads
-// the 16 bytes (32 elements) [32q, 32q + 32) of its row or column with one
-// 128-bit LDS read, and MFMA number s (0..3) of the step consumes elements
-// [32q + 8s, 32q + 8s + 8) from every lane group. A and B use the same
+// K permutation. Inside one 128-element K step, lane half h = lane / 32 reads
+// the 32 bytes (64 elements) [64h, 64h + 64) of its row or column with two
+// 128-bit LDS reads, and MFMA number s (0..7) of the step consumes elements
+// [64h + 8s, 64h + 8s + 8) from both halves. A and B use the same
 // permutation, and each 8-element run lies inside one 16-element scale group,
-// so every k is multiplied with its own partner exactly once.
+// so every k is multiplied with its own partner exactly once. The dequant of
+// substep s + 1 is issued before the MFMAs of substep s so that the VALU work
+// overlaps the matrix cores.
 //
 // Grouped scheduling. Tiles come from a device-built list (expert, first
 // sorted row, row count); the grid is sized for the worst case and idle
@@ -200,15 +202,23 @@ void gemm_kernel(GemmParams p) {
     };
 
     // ---- main loop ---------------------------------------------------------
+    // Wave (wm, wn) owns rows [128 wm, +128) and virtual columns [128 wn, +128)
+    // of the tile as 4 x 4 blocks of the 32 x 32 x 16 MFMA. Lane l serves row /
+    // column (l & 31) of a block and K half h = l >> 5: inside a 128-element K
+    // step it holds elements [64h, 64h + 64) (32 bytes, two 128-bit LDS reads),
+    // and substep s (0..7) feeds the MFMA elements [64h + 8s, 64h + 8s + 8),
+    // which lie in scale group 4h + s/2.
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int lr = lane & 15, q = lane >> 4;
+    const int l32 = lane & 31, h = lane >> 5;
 
-    float4_t acc[8][8];
+    float16_t acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     Stage st;
     load_stage(0, st);
@@ -220,33 +230,46 @@ void gemm_kernel(GemmParams p) {
         const bool more = ks + 1 < nk;
         if (more) load_stage(ks + 1, st);
 
-        u32x4 fa[8], fb[8];
-        uint32_t sa[8], sb[8];
+        u32x4 fa[4][2], fb[4][2];
+        uint32_t sa[4], sb[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = wm * 128 + 16 * i + lr;
-            fa[i] = *reinterpret_cast<const u32x4*>(&sm.a[buf][row * LDT + 16 * q]);
-            sa[i] = *reinterpret_cast<const uint16_t*>(&sm.asf[buf][row * 8 + 2 * q]);
+        for (int i = 0; i < 4; ++i) {
+            const int row = wm * 128 + 32 * i + l32;
+            const uint8_t* pa = &sm.a[buf][row * LDT + 32 * h];
+            fa[i][0] = *reinterpret_cast<const u32x4*>(pa);
+            fa[i][1] = *reinterpret_cast<const u32x4*>(pa + 16);
+            sa[i] = *reinterpret_cast<const uint32_t*>(&sm.asf[buf][row * 8 + 4 * h]);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int vc = wn * 128 + 16 * j + lr;
-            fb[j] = *reinterpret_cast<const u32x4*>(&sm.b[buf][vc * LDT + 16 * q]);
-            sb[j] = (uint32_t)sm.bsf[buf][(2 * q) * BN + vc] |
-                    ((uint32_t)sm.bsf[buf][(2 * q + 1) * BN + vc] << 8);
+        for (int j = 0; j < 4; ++j) {
+            const int vc = wn * 128 + 32 * j + l32;
+            const uint8_t* pb = &sm.b[buf][vc * LDT + 32 * h];
+            fb[j][0] = *reinterpret_cast<const u32x4*>(pb);
+            fb[j][1] = *reinterpret_cast<const u32x4*>(pb + 16);
+            const uint8_t* ps = &sm.bsf[buf][(4 * h) * BN + vc];
+            sb[j] = (uint32_t)ps[0] | ((uint32_t)ps[BN] << 8) | ((uint32_t)ps[2 * BN] << 16) |
+                    ((uint32_t)ps[3 * BN] << 24);
         }
+
+        half8_t ha[2][4], hb[2][4];
+        auto deq = [&](int s, half8_t (&xa)[4], half8_t (&xb)[4]) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8_t ha[8], hb[8];
+            for (int i = 0; i < 4; ++i)
+                xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
 #pragma unroll
-            for (int i = 0; i < 8; ++i) ha[i] = dequant8(fa[i][s], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
+            for (int j = 0; j < 4; ++j)
+                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
+        };
+        deq(0, ha[0], hb[0]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hb[j] = dequant8(fb[j][s], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
+        for (int s = 0; s < 8; ++s) {
+            if (s < 7) deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i], hb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[s & 1][i], hb[s & 1][j],
+                                                                        acc[i][j], 0, 0, 0);
         }
 
         if (more) store_stage(buf ^ 1, st);
@@ -254,24 +277,24 @@ void gemm_kernel(GemmParams p) {
     }
 
     // ---- epilogue ------------------------------------------------------------
-    // acc[i][j][r] = D[row 16i + 4q + r][col 16j + lr] of this wave's quadrant
+    // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
     const float alpha = p.a_gs[0] * p.b_alpha[expert];
     if (MODE == kGemmL1) {
-        // gate = virtual columns [0, 64) of the quadrant, up = [64, 128)
+        // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128)
         uint32_t amax_bits = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int local = wm * 128 + 16 * i + 4 * q + r;
+            for (int r = 0; r < 16; ++r) {
+                const int local = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (local >= row_count) continue;
                 const int64_t prow = row_start + local;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = (int64_t)nt * 128 + wn * 64 + 16 * j + lr;
+                for (int j = 0; j < 2; ++j) {
+                    const int64_t col = (int64_t)nt * 128 + wn * 64 + 32 * j + l32;
                     if (col >= p.I) continue;
                     const float g = bf16_to_f32(f32_to_bf16_rne(alpha * acc[i][j][r]));
-                    const float u = bf16_to_f32(f32_to_bf16_rne(alpha * acc[i][j + 4][r]));
+                    const float u = bf16_to_f32(f32_to_bf16_rne(alpha * acc[i][j + 2][r]));
                     // SiLU in float32; for g < 0 the form g e^g / (1 + e^g) keeps
                     // e^g finite where e^-g would overflow (g < -88)
                     float sil;
@@ -297,15 +320,15 @@ void gemm_kernel(GemmParams p) {
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int local = wm * 128 + 16 * i + 4 * q + r;
+            for (int r = 0; r < 16; ++r) {
+                const int local = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (local >= row_count) continue;
                 const int64_t prow = row_start + local;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int64_t col = (int64_t)nt * BN + wn * 128 + 16 * j + lr;
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + l32;
                     if (col >= N) continue;
                     const float v = alpha * acc[i][j][r];
                     if (MODE == kGemmL2) p.out_f32[prow * N + col] = v;
