@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnvfp4moe.so")
-SOURCES = ["api.hip", "quantize.hip", "route.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quantize.hip", "route.hip", "gemm.hip", "skinny.hip"]
 ARCH = "gfx950"
 
 

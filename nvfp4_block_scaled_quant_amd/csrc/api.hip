@@ -50,10 +50,15 @@ struct MoeLayout {
     int64_t max_tiles;
 };
 
-int64_t moe_max_tiles(int64_t S, int64_t E) {
+// Upper bound of sum_e ceil(count_e / BM): floor(S / BM) + number of non-empty experts.
+int64_t moe_max_tiles(int64_t S, int64_t E, int64_t BM) {
     if (S <= 0) return 0;
-    return S / kGemmBM + (E < S ? E : S);
+    return S / BM + (E < S ? E : S);
 }
+
+// Small batches (at most 16 slots per expert on average) stream the weights
+// with 16-row tiles; larger ones use the 256 x 256 MFMA tiles.
+bool moe_use_skinny(int64_t S, int64_t E) { return S <= (int64_t)kSkinnyBM * E; }
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     MoeLayout L;
@@ -69,7 +74,7 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     }
     L.amax = cur;
     cur = align_up(cur + 8);
-    L.max_tiles = moe_max_tiles(S, E);
+    L.max_tiles = moe_max_tiles(S, E, kSkinnyBM);     // the larger of the two tile lists
     L.tiles = cur;
     cur = align_up(cur + sizeof(Tile) * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
     L.num_tiles = cur;
@@ -238,6 +243,9 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     Tile* tiles = reinterpret_cast<Tile*>(ws + L.tiles);
     int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
     const int64_t S = T * topk;
+    const bool skinny = moe_use_skinny(S, E);
+    const int BM = skinny ? kSkinnyBM : kGemmBM;
+    const int64_t max_tiles = moe_max_tiles(S, E, BM);
 
     auto mark = [&](int i) -> hipError_t {
         return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
@@ -245,7 +253,7 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
 
     // 1. routing tables + tile list (also zeroes both amax slots)
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_ROUTE));
-    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, kGemmBM, counts, offsets, sorted_slot,
+    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
                            slot_row, tiles, num_tiles, amax, 2, stream));
     // 2. quantize x
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
@@ -267,11 +275,11 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     p1.b_alpha = w13_alpha;
     p1.tiles = tiles;
     p1.num_tiles = num_tiles;
-    p1.max_tiles = L.max_tiles;
+    p1.max_tiles = max_tiles;
     p1.out_bf16 = act;
     p1.I = I;
     p1.amax_slot = amax + 1;
-    NVFP4_TRY(launch_gemm(p1, stream));
+    NVFP4_TRY(skinny ? launch_skinny(p1, stream) : launch_gemm(p1, stream));
     // 4. requantize act (rows of valid slots only: offsets[E])
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_REQUANT));
     NVFP4_TRY(launch_quant_rows(act, S, I, offsets + E, amax + 1, aq, asf, gs2, stream));
@@ -289,9 +297,9 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     p2.b_alpha = w2_alpha;
     p2.tiles = tiles;
     p2.num_tiles = num_tiles;
-    p2.max_tiles = L.max_tiles;
+    p2.max_tiles = max_tiles;
     p2.out_f32 = o2;
-    NVFP4_TRY(launch_gemm(p2, stream));
+    NVFP4_TRY(skinny ? launch_skinny(p2, stream) : launch_gemm(p2, stream));
     // 5b. weighted combine
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_COMBINE));
     NVFP4_TRY(launch_combine(o2, slot_row, topk_weights, T, (int)topk, H, y, stream));

@@ -84,4 +84,8 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
+// Weight-streaming variant for tiles of at most kSkinnyBM rows (L1 / L2 only).
+constexpr int kSkinnyBM = 16;
+hipError_t launch_skinny(const GemmParams& p, hipStream_t s);
+
 }  // namespace nvfp4

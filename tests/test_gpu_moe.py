@@ -103,6 +103,17 @@ def test_ragged_shapes(nv, T, H, I, E, k):
     compare_layer(nv, make_layer(cfg), f"ragged T{T} H{H} I{I} E{E} k{k}")
 
 
+# shapes where slots per expert average at most 16 take the weight-streaming
+# path (16-row tiles): single rows, experts spanning several tiles, K tails
+@pytest.mark.parametrize("T,H,I,E,k", [(8, 256, 128, 8, 4), (60, 512, 256, 8, 2),
+                                       (20, 272, 144, 4, 2), (3, 1040, 400, 16, 5),
+                                       (33, 128, 16, 3, 1)])
+def test_small_batch_shapes(nv, T, H, I, E, k):
+    assert T * k <= 16 * E
+    cfg = W.small_layer(f"s{T}", T=T, H=H, I=I, E=E, topk=k, seed=3 * T + H + I)
+    compare_layer(nv, make_layer(cfg), f"small-batch T{T} H{H} I{I} E{E} k{k}")
+
+
 def test_skipped_ids_and_empty_experts(nv):
     cfg = W.small_layer("skip", T=90, H=256, I=128, E=6, topk=3, seed=9)
     L = make_layer(cfg)
