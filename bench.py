@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="skip the prefill timing (profiling runs of the decode batch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
     return ap.parse_args()
@@ -207,6 +209,13 @@ def main():
     t_setup = time.perf_counter()
     weights = make_weights(nv, cfg)
     setup_s = time.perf_counter() - t_setup
+    if args.decode_only:
+        dcfg = W.DECODE
+        dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, args.decode_steps, 5)
+        nbytes, touched = decode_bytes(dcfg, dids)
+        print(json.dumps({"workload": "decode", "us_per_step": dms * 1e3, "GBps": nbytes / (dms * 1e-3) / 1e9,
+                          "stage_us": {k: v * 1e3 for k, v in dstage.items()}, "finite": dfin}), flush=True)
+        return
     ms, stage_ms, s_valid, ids_np, finite = time_layer(nv, cfg, weights, args.steps, args.warmup)
     flops = 6.0 * s_valid * cfg.H * cfg.I
     l1_flops = 2.0 * s_valid * cfg.H * 2 * cfg.I
