@@ -35,6 +35,69 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// float64 -> bf16 bits, nearest-even, in effect one rounding: rounding to
+// float32 toward zero and setting the last bit when inexact (round to odd)
+// keeps enough information for the second rounding to be exact.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+    const float t = __double2float_rz(v);
+    uint32_t tb = __float_as_uint(t);
+    if ((double)t != v) tb |= 1u;
+    return f32_to_bf16_rne(__uint_as_float(tb));
+}
+
+// e^x in float64 (Cody-Waite reduction x = n ln2 + r, |r| <= ln2/2, with ln2
+// split into a 32-bit head, so n * head is exact, and a tail; e^r from its
+// Taylor series to degree 13, truncation below 2^-60 relative; then 2^n).
+// About one ulp; inputs are clamped to [-800, 800], where the result is
+// already 0 or infinity.
+__device__ __forceinline__ double exp_f64(double x) {
+    x = fmin(fmax(x, -800.0), 800.0);
+    const double n = __builtin_rint(x * 1.4426950408889634);
+    double r = __builtin_fma(-n, 0.6931471803691238, x);
+    r = __builtin_fma(-n, 1.9082149292705877e-10, r);
+    double p = 1.6059043836821613e-10;
+    p = __builtin_fma(p, r, 2.08767569878681e-09);
+    p = __builtin_fma(p, r, 2.505210838544172e-08);
+    p = __builtin_fma(p, r, 2.755731922398589e-07);
+    p = __builtin_fma(p, r, 2.7557319223985893e-06);
+    p = __builtin_fma(p, r, 2.48015873015873e-05);
+    p = __builtin_fma(p, r, 0.0001984126984126984);
+    p = __builtin_fma(p, r, 0.001388888888888889);
+    p = __builtin_fma(p, r, 0.008333333333333333);
+    p = __builtin_fma(p, r, 0.041666666666666664);
+    p = __builtin_fma(p, r, 0.16666666666666666);
+    p = __builtin_fma(p, r, 0.5);
+    p = __builtin_fma(p, r, 1.0);
+    p = __builtin_fma(p, r, 1.0);
+    return __builtin_ldexp(p, (int)n);
+}
+
+// act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
+// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
+// A float32 evaluation (relative error a few ulps) decides the rounding when
+// it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
+// e^g leaves the float32 normal range, the product is recomputed in float64.
+// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
+// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
+// would round the wrong way.)
+__device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
+    if (g >= -87.0f) {
+        // silu(g) = g / (1 + e^-g) = g e^g / (1 + e^g); one exponential of -|g|
+        // serves both signs. Error: expf and the fast division a couple of ulps
+        // each, the products half an ulp: well inside the 32-ulp margin below.
+        const float e = expf(-fabsf(g));
+        const float num = (g >= 0.0f) ? g : g * e;
+        const float v = __fdividef(num, 1.0f + e) * u;
+        const uint32_t b = __float_as_uint(v);
+        const uint32_t low = b & 0xFFFFu;
+        const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
+        if ((b & 0x7F800000u) != 0u && (b & 0x7F800000u) != 0x7F800000u && dist > 32u)
+            return f32_to_bf16_rne(v);
+    }
+    const double gd = g, ud = u;
+    return f64_to_bf16_rne((gd / (1.0 + exp_f64(-gd))) * ud);
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4 quantization arithmetic. Every operation is one IEEE float32 operation
 // with round-to-nearest-even; divisions are the correctly rounded ones (the

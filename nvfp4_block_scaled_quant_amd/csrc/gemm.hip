@@ -280,35 +280,39 @@ void gemm_kernel(GemmParams p) {
     // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
     const float alpha = p.a_gs[0] * p.b_alpha[expert];
     if (MODE == kGemmL1) {
-        // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128)
+        // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
+        // The rounded (gate, up) pairs of one half of the tile (128 rows x 128
+        // act columns) go through the now idle LDS; then all threads apply
+        // SiLU and store act row by row (coalesced), in two halves.
+        uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [128][128] g | u << 16
         uint32_t amax_bits = 0;
+        for (int half = 0; half < 2; ++half) {
+            if (wm == half) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int local = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (local >= row_count) continue;
-                const int64_t prow = row_start + local;
+                    for (int r = 0; r < 16; ++r)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int64_t col = (int64_t)nt * 128 + wn * 64 + 32 * j + l32;
-                    if (col >= p.I) continue;
-                    const float g = bf16_to_f32(f32_to_bf16_rne(alpha * acc[i][j][r]));
-                    const float u = bf16_to_f32(f32_to_bf16_rne(alpha * acc[i][j + 2][r]));
-                    // SiLU in float32; for g < 0 the form g e^g / (1 + e^g) keeps
-                    // e^g finite where e^-g would overflow (g < -88)
-                    float sil;
-                    if (g >= 0.0f) {
-                        sil = g / (1.0f + expf(-g));
-                    } else {
-                        const float e = expf(g);
-                        sil = (g * e) / (1.0f + e);
-                    }
-                    const uint32_t a = f32_to_bf16_rne(sil * u);
-                    p.out_bf16[prow * p.I + col] = (uint16_t)a;
+                        for (int j = 0; j < 2; ++j) {
+                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const int col = wn * 64 + 32 * j + l32;
+                            const uint32_t g = f32_to_bf16_rne(alpha * acc[i][j][r]);
+                            const uint32_t u = f32_to_bf16_rne(alpha * acc[i][j + 2][r]);
+                            gu[row * 128 + col] = g | (u << 16);
+                        }
+            }
+            __syncthreads();
+            for (int e = tid; e < 128 * 128; e += NT) {
+                const int local = half * 128 + (e >> 7);
+                const int64_t col = (int64_t)nt * 128 + (e & 127);
+                if (local < row_count && col < p.I) {
+                    const uint32_t w = gu[e];
+                    const uint32_t a = silu_mul_bf16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
+                    p.out_bf16[(int64_t)(row_start + local) * p.I + col] = (uint16_t)a;
                     amax_bits = max(amax_bits, a & 0x7FFFu);
                 }
             }
+            __syncthreads();
         }
         __shared__ uint32_t red[NT / 64];
         amax_bits = wave_max_u32(amax_bits);

@@ -203,14 +203,7 @@ void skinny_kernel(GemmParams p, int a_pitch, int sf_pitch) {
             for (int e = 0; e < 2; ++e) {
                 const float g = bf16_to_f32(f32_to_bf16_rne(alpha * sum[f + e]));
                 const float u = bf16_to_f32(f32_to_bf16_rne(alpha * sum[f + e + 8]));
-                float sil;
-                if (g >= 0.0f) {
-                    sil = g / (1.0f + expf(-g));
-                } else {
-                    const float ex = expf(g);
-                    sil = (g * ex) / (1.0f + ex);
-                }
-                const uint32_t a = f32_to_bf16_rne(sil * u);
+                const uint32_t a = silu_mul_bf16(g, u);
                 amax_bits = row_ok ? max(amax_bits, a & 0x7FFFu) : amax_bits;
                 two |= a << (16 * e);
             }

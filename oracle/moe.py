@@ -52,8 +52,33 @@ def slots_by_expert(topk_ids, num_experts):
     return out
 
 
+def _l1_expert(task):
+    """L1 rows of one expert and the SiLU half of stage 4 (R1, R2)."""
+    xq_rows, xsf_rows, w13q_e, w13sf_e, alpha, I, keep = task
+    a = dequantize_rows(xq_rows, xsf_rows)
+    b = dequantize_cols(w13q_e, w13sf_e)
+    gu_f64 = alpha * (a @ b)
+    gu = bf16_from_f64(gu_f64)                                       # R1
+    g = bf16_to_f32(gu[:, :I]).astype(np.float64)
+    u = bf16_to_f32(gu[:, I:]).astype(np.float64)
+    return bf16_from_f64(silu(g) * u), (gu_f64 if keep else None)    # R2
+
+
+def _l2_expert(task):
+    """Weighted L2 rows of one expert, float64."""
+    aq_rows, asf_rows, w2q_e, w2sf_e, alpha, w = task
+    a = dequantize_rows(aq_rows, asf_rows)
+    b = dequantize_cols(w2q_e, w2sf_e)
+    return w[:, None] * (alpha * (a @ b))
+
+
+def _map(fn, tasks, pool):
+    """Per-expert work, in order; `pool` (anything with .map) spreads it."""
+    return pool.map(fn, tasks) if pool is not None else [fn(t) for t in tasks]
+
+
 def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
-                w2q, w2sf, w2_alpha, keep=False):
+                w2q, w2sf, w2_alpha, keep=False, pool=None):
     """Reference layer output.
 
     Shapes: x_bits (T, H) uint16 bf16 bits; topk_ids (T, k) int; topk_weights
@@ -64,6 +89,9 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     set, the per-slot intermediates indexed [t, j]: gu (float64, unrounded),
     act_bits (bf16, T x k x I), aq, asf, contrib (weighted L2 rows, float64),
     valid mask, plus xq, xsf, gs1, gs2.
+
+    `pool` (e.g. a multiprocessing pool) only distributes the per-expert GEMMs;
+    the arithmetic is the same with or without it.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     ids = np.asarray(topk_ids).astype(np.int64)
@@ -83,19 +111,14 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     # stage 3 + the SiLU half of stage 4
     act_bits = np.zeros((T, k, I), dtype=np.uint16)
     gu_keep = np.zeros((T, k, 2 * I), dtype=np.float64) if keep else None
-    for e, (t_idx, j_idx) in enumerate(groups):
-        if t_idx.size == 0:
-            continue
-        a = dequantize_rows(xq[t_idx], xsf[t_idx])
-        b = dequantize_cols(w13q[e], w13sf[e])
-        alpha = np.float64(gs1) * np.float64(np.float32(w13_alpha[e]))
-        gu_f64 = alpha * (a @ b)
+    tasks = [(xq[t_idx], xsf[t_idx], w13q[e], w13sf[e],
+              np.float64(gs1) * np.float64(np.float32(w13_alpha[e])), I, keep)
+             for e, (t_idx, j_idx) in enumerate(groups) if t_idx.size]
+    placed = [(t_idx, j_idx) for t_idx, j_idx in groups if t_idx.size]
+    for (t_idx, j_idx), (act_e, gu_e) in zip(placed, _map(_l1_expert, tasks, pool)):
+        act_bits[t_idx, j_idx] = act_e
         if keep:
-            gu_keep[t_idx, j_idx] = gu_f64
-        gu = bf16_from_f64(gu_f64)                                   # R1
-        g = bf16_to_f32(gu[:, :I]).astype(np.float64)
-        u = bf16_to_f32(gu[:, I:]).astype(np.float64)
-        act_bits[t_idx, j_idx] = bf16_from_f64(silu(g) * u)          # R2
+            gu_keep[t_idx, j_idx] = gu_e
 
     # the requantization half of stage 4: one gs2 over all valid slots
     t_all, j_all = np.nonzero(valid)
@@ -111,13 +134,11 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     # stage 5: L2 and the weighted combine, float64 until the final rounding
     y = np.zeros((T, H), dtype=np.float64)
     contrib = np.zeros((T, k, H), dtype=np.float64)
-    for e, (t_idx, j_idx) in enumerate(groups):
-        if t_idx.size == 0:
-            continue
-        a = dequantize_rows(aq[t_idx, j_idx], asf[t_idx, j_idx])
-        b = dequantize_cols(w2q[e], w2sf[e])
-        alpha = np.float64(gs2) * np.float64(np.float32(w2_alpha[e]))
-        contrib[t_idx, j_idx] = wts[t_idx, j_idx][:, None] * (alpha * (a @ b))
+    tasks = [(aq[t_idx, j_idx], asf[t_idx, j_idx], w2q[e], w2sf[e],
+              np.float64(gs2) * np.float64(np.float32(w2_alpha[e])), wts[t_idx, j_idx])
+             for e, (t_idx, j_idx) in enumerate(groups) if t_idx.size]
+    for (t_idx, j_idx), rows in zip(placed, _map(_l2_expert, tasks, pool)):
+        contrib[t_idx, j_idx] = rows
     for j in range(k):                                               # j order
         y += contrib[:, j, :]
     out = {"y": y, "y_bits": bf16_from_f64(y), "gs1": gs1, "gs2": np.float32(gs2)}

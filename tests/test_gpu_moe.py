@@ -9,9 +9,9 @@ from helpers import (bf16_ulp_distance, check_bf16_output, cosine, make_layer,
 pytestmark = pytest.mark.gpu
 
 
-def compare_layer(nv, L, label, min_act_exact=0.995):
+def compare_layer(nv, L, label, min_act_exact=0.995, pool=None):
     g = run_gpu_layer(nv, L)
-    r = run_oracle_layer(L)
+    r = run_oracle_layer(L, pool=pool)
     T, k = L["ids"].shape
     E = L["w13q"].shape[0]
     S = T * k
@@ -73,19 +73,35 @@ def compare_layer(nv, L, label, min_act_exact=0.995):
             # only possible if the act element holding the maximum differs
             assert not same.all(), f"{label}: gs2 differs although act matches"
 
-    # stage 5: y. Faithful rounding is required for every token whose slots'
-    # act rows all equal the oracle's (then L2 and the combine see identical
-    # quantized inputs); elsewhere a flipped act ulp may flip a requantized
-    # nibble and only the benchmark spec bound applies.
+    # stage 5: y. Tokens whose slots' quantized act rows (bytes and scale
+    # bytes) all equal the oracle's, with the same gs2, feed identical inputs
+    # to L2 and the combine, so their y is unique: the benchmark spec bound and
+    # faithful rounding apply. Where a gate/up value sits within float32
+    # accumulation noise of a bf16 midpoint both roundings are valid; a
+    # resulting flipped requantized nibble moves y by up to a few 1e-3 of
+    # max|y| (one E2M1 step of a block near the act amax). Such tokens must be
+    # few and still close (cosine, loose bound).
     tok_ok = np.ones(T, bool)
     if nvalid:
-        row_ok = same.all(axis=1)
-        tok_ok[t_of[~row_ok]] = False
+        q_same = ((g["aq"][:nvalid] == r["aq"][t_of, j_of]).all(axis=1) &
+                  (g["asf"][:nvalid] == r["asf"][t_of, j_of]).all(axis=1))
+        tok_ok[t_of[~q_same]] = False
         if g["gs2"].view(np.uint32) != np.float32(r["gs2"]).view(np.uint32):
             tok_ok[:] = False
-    st = check_bf16_output(g["y"], r["y"], f"{label}: y", min_exact=0.98, faithful_rows=tok_ok)
-    st["faithful_tokens"] = float(tok_ok.mean())
-    assert st["cos"] >= 0.9999, f"{label}: cosine {st['cos']}"
+    st = check_bf16_output(g["y"], r["y"], f"{label}: y", min_exact=0.98, faithful_rows=tok_ok,
+                           bound_rows=tok_ok)
+    st["unique_tokens"] = float(tok_ok.mean())
+    beyond = st.pop("beyond_rounding_rows")
+    if (~tok_ok).any():
+        from oracle.formats import bf16_to_f32
+        yg = bf16_to_f32(g["y"]).astype(np.float64)
+        cos_t = [cosine(yg[t], r["y"][t]) for t in np.nonzero(~tok_ok)[0]]
+        st["other_tokens_min_cos"] = float(min(cos_t))
+        st["other_tokens_max_beyond"] = float(beyond[~tok_ok].max())
+        assert min(cos_t) >= 0.999, f"{label}: token cosine {min(cos_t)}"
+        assert beyond[~tok_ok].max() <= 1e-2, f"{label}: {beyond[~tok_ok].max()}"
+        if g["gs2"].view(np.uint32) == np.float32(r["gs2"]).view(np.uint32):
+            assert (~tok_ok).sum() <= max(2, 0.05 * T), f"{label}: {(~tok_ok).sum()} tokens differ"
     st["act_exact"] = act_exact
     print(label, st)
     return g, r, st
