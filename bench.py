@@ -64,28 +64,33 @@ def to_dev(a):
 
 
 def make_weights(nv, cfg):
-    """Per-expert bf16 weights from the workload recipe, quantized on the GPU."""
+    """Per-expert bf16 weights from the workload recipe, quantized on the GPU
+    (canonical layout) and prepacked once into the layout the GEMMs read."""
     import torch
     import workloads as W
     E, H, I = cfg.E, cfg.H, cfg.I
-    w13q = torch.empty((E, H // 2, 2 * I), dtype=torch.uint8, device="cuda")
-    w13sf = torch.empty((E, H // 16, 2 * I), dtype=torch.uint8, device="cuda")
-    w2q = torch.empty((E, I // 2, H), dtype=torch.uint8, device="cuda")
-    w2sf = torch.empty((E, I // 16, H), dtype=torch.uint8, device="cuda")
+    qh, sh = nv.operand_pitches(H)
+    qi, si = nv.operand_pitches(I)
+    w13 = torch.empty((E, 2 * I, qh), dtype=torch.uint8, device="cuda")
+    w13sf = torch.empty((E, 2 * I, sh), dtype=torch.uint8, device="cuda")
+    w2 = torch.empty((E, H, qi), dtype=torch.uint8, device="cuda")
+    w2sf = torch.empty((E, H, si), dtype=torch.uint8, device="cuda")
     w13a = torch.empty((E,), dtype=torch.float32, device="cuda")
     w2a = torch.empty((E,), dtype=torch.float32, device="cuda")
     for e in range(E):
-        w13, w2 = W.expert_weights_bf16(cfg, e)
-        q, sf, a = nv.quantize_weights(to_dev(w13)[None])
-        w13q[e], w13sf[e], w13a[e] = q[0], sf[0], a[0]
-        q, sf, a = nv.quantize_weights(to_dev(w2)[None])
-        w2q[e], w2sf[e], w2a[e] = q[0], sf[0], a[0]
+        w13_bf16, w2_bf16 = W.expert_weights_bf16(cfg, e)
+        q, sf, a = nv.quantize_weights(to_dev(w13_bf16)[None])
+        q_t, sf_t = nv.prepack_weights(q, sf)
+        w13[e], w13sf[e], w13a[e] = q_t[0], sf_t[0], a[0]
+        q, sf, a = nv.quantize_weights(to_dev(w2_bf16)[None])
+        q_t, sf_t = nv.prepack_weights(q, sf)
+        w2[e], w2sf[e], w2a[e] = q_t[0], sf_t[0], a[0]
     if cfg.alpha_loguniform:
         a13, a2 = W.alphas_loguniform(cfg)
         w13a.copy_(torch.from_numpy(a13))
         w2a.copy_(torch.from_numpy(a2))
     torch.cuda.synchronize()
-    return w13q, w13sf, w13a, w2q, w2sf, w2a
+    return w13, w13sf, w13a, w2, w2sf, w2a
 
 
 def time_layer(nv, cfg, weights, steps, warmup):

@@ -17,16 +17,25 @@
  *     It is kept out of the E4M3 bytes and enters the GEMMs as alpha.
  *   - dequantized element = e2m1(nibble) * e4m3(scale byte) * global scale.
  *
- * Layouts (all row-major, densely packed, no padding):
+ * Layouts (all row-major):
  *   activation   x        (M, K) bf16 (uint16 bit patterns)
  *   quantized A  q        (M, K/2) bytes, packed along K
  *                sf       (M, K/16) E4M3 bytes, sf[m][g] covers k in [16g, 16g+16)
- *   weights      w        (E, K/2, N) bytes, packed along K: byte [e][kh][n]
- *                         holds W[2kh][n] (low) and W[2kh+1][n] (high)
+ *   canonical    w        (E, K/2, N) bytes, packed along K: byte [e][kh][n]
+ *   weights               holds W[2kh][n] (low) and W[2kh+1][n] (high)
  *                w_sf     (E, K/16, N) E4M3 bytes
  *                w_alpha  (E) float32 weight global scales (dequant direction)
+ *   packed       w_t      (E, N, pitch_q(K)) bytes: row n of matrix e holds
+ *   weights               column n of W[e], packed along K like an A row
+ *                         (byte kh = W[2kh][n] | W[2kh+1][n] << 4), zero-padded
+ *                w_sf_t   (E, N, pitch_sf(K)) E4M3 bytes, zero-padded
+ *   pitch_q(K)  = K/2 rounded up to a multiple of 64 bytes (a 128-element step)
+ *   pitch_sf(K) = K/16 rounded up to a multiple of 8 bytes
+ *   The packed weights are the canonical ones with every matrix byte-transposed
+ *   (the pages' GEMM took its weight operand column-major); they are made once,
+ *   at load time, by nvfp4_prepack_weights and are what the GEMMs read.
  *   w13 is the plain concatenation [gate; up] along N: columns [0, I) are the
- *   gate projection, [I, 2I) the up projection.
+ *   gate projection, [I, 2I) the up projection (rows [0, I) / [I, 2I) packed).
  *
  * Ownership and execution. Every pointer argument is a DEVICE pointer unless
  * its comment says host. The caller owns all memory, including workspaces; the
@@ -108,18 +117,42 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * nvfp4_operand_pitches - the padded row pitches of the packed weight layout
+ * (and of the quantized operands inside the expert layer's workspace).
+ *   K > 0, K % 16 == 0; ldq, ldsf: host int64 out (pitch_q(K), pitch_sf(K)).
+ * ------------------------------------------------------------------------ */
+int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_prepack_weights - canonical (K-packed, N fastest) quantized weights to
+ * the packed layout the GEMMs read (one byte transpose per matrix, padding
+ * bytes written as zero). A pure data movement, no arithmetic.
+ *
+ *   w (E, K/2, N), w_sf (E, K/16, N): canonical bytes (nvfp4_quantize_weights)
+ *   w_t (E, N, pitch_q(K)), w_sf_t (E, N, pitch_sf(K)): packed out, separate
+ *   buffers (no in-place), w_t 16-byte and w_sf_t 8-byte aligned.
+ *   K % 16 == 0, E <= 65535. E == 0 is valid and enqueues nothing.
+ * ------------------------------------------------------------------------ */
+int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int64_t K, int64_t N,
+                          uint8_t* w_t, uint8_t* w_sf_t, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * nvfp4_gemm - block-scaled NVFP4 GEMM, one expert
  * (DEBUG_LOG, "NVFP4 MoE Pipeline": GEMM with alpha = igs * weight global).
  *
  *   out[m][n] = bf16( (a_gs[0] * b_alpha[0]) * sum_k deqA[m][k] * deqB[k][n] )
  *
- *   aq (M, K/2), asf (M, K/16): the quantized activation (nvfp4_quantize)
+ *   aq (M, K/2), asf (M, K/16): the quantized activation (nvfp4_quantize),
+ *           aq 16-byte and asf 8-byte aligned
  *   a_gs    one float32, the activation's global scale
- *   bq (K/2, N), bsf (K/16, N): K-packed weight; b_alpha one float32
+ *   bq (N, K/2), bsf (N, K/16): one packed weight matrix (nvfp4_prepack_weights
+ *           with E = 1; for K % 128 == 0 the pitches are exactly K/2 and K/16),
+ *           bq 16-byte and bsf 8-byte aligned
+ *   b_alpha one float32
  *   out (M, N) bf16
  * Products of dequantized elements are exact; the sum is float32; the alpha
  * product and its multiply are float32; the one bf16 rounding is the last step.
- * K % 16 == 0, N % 16 == 0. No workspace.
+ * K % 128 == 0, N % 16 == 0, M * K/2 and N * K/2 below 2^31. No workspace.
  * ------------------------------------------------------------------------ */
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
                const uint8_t* bq, const uint8_t* bsf, const float* b_alpha,
@@ -140,10 +173,15 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *   x             (T, H) bf16
  *   topk_ids      (T, topk) int32
  *   topk_weights  (T, topk) float32, used as given (no renormalization)
- *   w13 (E, H/2, 2I), w13_sf (E, H/16, 2I), w13_alpha (E)
- *   w2  (E, I/2, H),  w2_sf  (E, I/16, H),  w2_alpha  (E)
+ *   w13 (E, 2I, pitch_q(H)), w13_sf (E, 2I, pitch_sf(H)), w13_alpha (E)
+ *   w2  (E, H, pitch_q(I)),  w2_sf  (E, H, pitch_sf(I)),  w2_alpha  (E)
+ *                 packed weights (nvfp4_prepack_weights of the canonical
+ *                 (E, H/2, 2I) and (E, I/2, H) tensors); w13, w2 16-byte and
+ *                 the scale tensors 8-byte aligned
  *   y             (T, H) bf16 out
- *   H % 16 == 0, I % 16 == 0, 1 <= topk <= E, T >= 0.
+ *   H % 16 == 0, I % 16 == 0, 1 <= topk <= E, T >= 0; each of
+ *   2I * pitch_q(H), H * pitch_q(I), T * pitch_q(H), T * topk * pitch_q(I)
+ *   below 2^31 (32-bit buffer offsets), else NVFP4_ESHAPE.
  *
  * Workspace: nvfp4_moe_workspace(T, H, I, E, topk) bytes, 256-byte aligned.
  * The intermediates stay in the workspace after the call; their byte offsets
@@ -167,8 +205,8 @@ enum {
 
 /* Offsets (bytes from the workspace base) of the intermediates, indexed by: */
 enum {
-    NVFP4_MOE_WS_XQ = 0,            /* (T, H/2) bytes */
-    NVFP4_MOE_WS_XSF = 1,           /* (T, H/16) bytes */
+    NVFP4_MOE_WS_XQ = 0,            /* (T, pitch_q(H)) bytes, row t's first H/2 are x's */
+    NVFP4_MOE_WS_XSF = 1,           /* (T, pitch_sf(H)) bytes, first H/16 used */
     NVFP4_MOE_WS_GS1 = 2,           /* float32 */
     NVFP4_MOE_WS_GS2 = 3,           /* float32 */
     NVFP4_MOE_WS_COUNTS = 4,        /* int32 (E): valid slots per expert */
@@ -176,8 +214,8 @@ enum {
     NVFP4_MOE_WS_SORTED_SLOT = 6,   /* int32 (S): slot t*topk+j of each sorted row */
     NVFP4_MOE_WS_SLOT_ROW = 7,      /* int32 (S): sorted row of each slot, -1 if skipped */
     NVFP4_MOE_WS_ACT = 8,           /* bf16 (S, I), sorted rows */
-    NVFP4_MOE_WS_AQ = 9,            /* (S, I/2) bytes, sorted rows */
-    NVFP4_MOE_WS_ASF = 10,          /* (S, I/16) bytes, sorted rows */
+    NVFP4_MOE_WS_AQ = 9,            /* (S, pitch_q(I)) bytes, sorted rows, first I/2 used */
+    NVFP4_MOE_WS_ASF = 10,          /* (S, pitch_sf(I)) bytes, sorted rows, first I/16 used */
     NVFP4_MOE_WS_O2 = 11,           /* float32 (S, H), sorted rows, weight not applied */
     NVFP4_MOE_WS_NUM = 12
 };

@@ -5,8 +5,10 @@ kernels. PyTorch provides device memory and the current stream. The functions
 mirror the C ABI in include/nvfp4moe.h:
 
     quantize(x)                      -> (q, sf, gs)
-    quantize_weights(w)              -> (q, sf, alpha)
-    gemm(aq, asf, a_gs, bq, bsf, b_alpha) -> out (bf16)
+    quantize_weights(w)              -> (q, sf, alpha)    canonical weight layout
+    operand_pitches(K)               -> (ldq, ldsf)
+    prepack_weights(q, sf)           -> (q_t, sf_t)       packed layout the GEMMs read
+    gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
     moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
                 w2, w2_sf, w2_alpha, workspace=None, stage_events=None) -> y
 
@@ -24,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4moe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m nvfp4_block_scaled_quant_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python nvfp4_block_scaled_quant_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -37,6 +39,8 @@ _SIGS = {
     "nvfp4_quantize": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "nvfp4_quantize_weights_workspace": ([_i64, _i64, _i64], _sz),
     "nvfp4_quantize_weights": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nvfp4_operand_pitches": ([_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
+    "nvfp4_prepack_weights": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "nvfp4_gemm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
     "nvfp4_moe_workspace": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_moe_workspace_layout": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
@@ -128,16 +132,44 @@ def quantize_weights(w):
     return q, sf, alpha
 
 
+def operand_pitches(K):
+    """Row pitches (bytes) of the packed weight layout for reduction length K:
+    (K/2 rounded up to 64, K/16 rounded up to 8)."""
+    ldq, ldsf = _i64(), _i64()
+    _check(_lib.nvfp4_operand_pitches(K, ctypes.byref(ldq), ctypes.byref(ldsf)),
+           "nvfp4_operand_pitches")
+    return ldq.value, ldsf.value
+
+
+def prepack_weights(q, sf):
+    """Canonical quantized weights q (E, K/2, N), sf (E, K/16, N) -> the packed
+    layout (E, N, pitch_q(K)), (E, N, pitch_sf(K)) that gemm and moe_forward read."""
+    _need(q, torch.uint8, "q", 3)
+    _need(sf, torch.uint8, "sf", 3)
+    E, Kh, N = q.shape
+    K = 2 * Kh
+    if sf.shape != (E, K // 16, N):
+        raise ValueError("prepack_weights: q and sf shapes do not match")
+    ldq, ldsf = operand_pitches(K)
+    q_t = torch.empty((E, N, ldq), dtype=torch.uint8, device=q.device)
+    sf_t = torch.empty((E, N, ldsf), dtype=torch.uint8, device=q.device)
+    _check(_lib.nvfp4_prepack_weights(_ptr(q), _ptr(sf), E, K, N, _ptr(q_t), _ptr(sf_t),
+                                      _stream()), "nvfp4_prepack_weights")
+    return q_t, sf_t
+
+
 def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
-    """Block-scaled NVFP4 GEMM: (M, K/2)+(M, K/16) x (K/2, N)+(K/16, N) -> bf16 (M, N)."""
+    """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times the
+    packed weight bq (N, K/2) + bsf (N, K/16) -> bf16 (M, N). K % 128 == 0."""
     for t, n, d in ((aq, "aq", torch.uint8), (asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
                     (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
                     (b_alpha, "b_alpha", torch.float32)):
         _need(t, d, n)
     M = aq.shape[0]
     K = aq.shape[1] * 2
-    N = bq.shape[1]
-    if bq.shape[0] * 2 != K or asf.shape != (M, K // 16) or bsf.shape != (K // 16, N):
+    N = bq.shape[0]
+    if (aq.dim() != 2 or bq.dim() != 2 or bq.shape[1] * 2 != K or asf.shape != (M, K // 16)
+            or bsf.shape != (N, K // 16)):
         raise ValueError("operand shapes do not match")
     out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device) if out is None else out
     _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),
@@ -160,7 +192,9 @@ def moe_workspace_layout(T, H, I, E, topk):
 
 def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
                 y=None, workspace=None, stage_events=None):
-    """The five-stage NVFP4 expert layer. Shapes as in include/nvfp4moe.h.
+    """The five-stage NVFP4 expert layer. Weights in the packed layout
+    (prepack_weights): w13 (E, 2I, pitch_q(H)), w13_sf (E, 2I, pitch_sf(H)),
+    w2 (E, H, pitch_q(I)), w2_sf (E, H, pitch_sf(I)).
 
     stage_events: None or a StageEvents; returns y (T, H) bf16.
     """
@@ -174,9 +208,13 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     T, H = x.shape
     topk = topk_ids.shape[1]
     E = w13.shape[0]
-    I = w2.shape[1] * 2
-    if (w13.shape != (E, H // 2, 2 * I) or w13_sf.shape != (E, H // 16, 2 * I)
-            or w2.shape != (E, I // 2, H) or w2_sf.shape != (E, I // 16, H)
+    I = w13.shape[1] // 2
+    if H % 16 or I % 16 or I == 0:
+        raise ValueError("moe_forward: H and I must be positive multiples of 16")
+    ldq_h, ldsf_h = operand_pitches(H)
+    ldq_i, ldsf_i = operand_pitches(I)
+    if (w13.shape != (E, 2 * I, ldq_h) or w13_sf.shape != (E, 2 * I, ldsf_h)
+            or w2.shape != (E, H, ldq_i) or w2_sf.shape != (E, H, ldsf_i)
             or w13_alpha.shape != (E,) or w2_alpha.shape != (E,)
             or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
         raise ValueError("moe_forward: inconsistent shapes")

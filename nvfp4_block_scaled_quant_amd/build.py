@@ -1,6 +1,6 @@
 """Build libnvfp4moe.so in-tree with hipcc for gfx950.
 
-    python -m nvfp4_block_scaled_quant_amd.build
+    python nvfp4_block_scaled_quant_amd/build.py
 
 Every HIP source is compiled with:
   -ffp-contract=off                          the quantizer's float32 steps must

@@ -63,10 +63,11 @@ bool moe_use_skinny(int64_t S, int64_t E) { return S <= (int64_t)kSkinnyBM * E; 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     MoeLayout L;
     const int64_t S = T * topk;
+    // quantized GEMM operands use the padded row pitches pitch_q / pitch_sf
     const size_t sizes[NVFP4_MOE_WS_NUM] = {
-        (size_t)(T * H / 2),  (size_t)(T * H / 16), 4, 4,
+        (size_t)(T * pitch_q(H)), (size_t)(T * pitch_sf(H)), 4, 4,
         (size_t)(4 * E),      (size_t)(4 * (E + 1)), (size_t)(4 * S), (size_t)(4 * S),
-        (size_t)(2 * S * I),  (size_t)(S * I / 2),  (size_t)(S * I / 16), (size_t)(4 * S * H)};
+        (size_t)(2 * S * I),  (size_t)(S * pitch_q(I)), (size_t)(S * pitch_sf(I)), (size_t)(4 * S * H)};
     size_t cur = 0;
     for (int i = 0; i < NVFP4_MOE_WS_NUM; ++i) {
         L.off[i] = cur;
@@ -107,7 +108,7 @@ const char* nvfp4_strerror(int status) {
     }
 }
 
-int nvfp4_version(void) { return (1 << 16) | 0; }
+int nvfp4_version(void) { return (2 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -130,7 +131,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t*
     uint32_t* slot = static_cast<uint32_t*>(workspace);
     NVFP4_TRY(launch_zero_u32(slot, 1, stream));
     NVFP4_TRY(launch_amax_bf16(x, M * K, slot, stream));
-    NVFP4_TRY(launch_quant_rows(x, M, K, nullptr, slot, q, sf, gs, stream));
+    NVFP4_TRY(launch_quant_rows(x, M, K, nullptr, slot, q, K / 2, sf, K / 16, gs, stream));
     return NVFP4_OK;
 }
 
@@ -162,16 +163,41 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N, u
 }
 
 // ---------------------------------------------------------------------------
+int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf) {
+    if (K <= 0) return NVFP4_EINVAL;
+    if (K % 16) return NVFP4_ESHAPE;
+    if (!ldq || !ldsf) return NVFP4_EINVAL;
+    *ldq = pitch_q(K);
+    *ldsf = pitch_sf(K);
+    return NVFP4_OK;
+}
+
+int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int64_t K, int64_t N,
+                          uint8_t* w_t, uint8_t* w_sf_t, hipStream_t stream) {
+    if (E < 0 || K <= 0 || N <= 0) return NVFP4_EINVAL;
+    if (K % 16 || E > 65535) return NVFP4_ESHAPE;
+    if (E == 0) return NVFP4_OK;
+    if (!w || !w_sf || !w_t || !w_sf_t) return NVFP4_EINVAL;
+    if (!aligned(w_t, 16) || !aligned(w_sf_t, 8)) return NVFP4_EINVAL;
+    int dv = check_device();
+    if (dv) return dv;
+    NVFP4_TRY(launch_transpose_bytes(w, E, K / 2, N, w_t, pitch_q(K), stream));
+    NVFP4_TRY(launch_transpose_bytes(w_sf, E, K / 16, N, w_sf_t, pitch_sf(K), stream));
+    return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const uint8_t* bq,
                const uint8_t* bsf, const float* b_alpha, int64_t M, int64_t N, int64_t K,
                uint16_t* out, hipStream_t stream) {
     if (M < 0 || N <= 0 || K <= 0) return NVFP4_EINVAL;
-    if (K % 16 || N % 16) return NVFP4_ESHAPE;
+    if (K % 128 || N % 16) return NVFP4_ESHAPE;
     if (M == 0) return NVFP4_OK;
     if (!aq || !asf || !a_gs || !bq || !bsf || !b_alpha || !out) return NVFP4_EINVAL;
-    if (!aligned(aq, 8) || !aligned(bq, 4) || !aligned(bsf, 8) || !aligned(out, 2) ||
-        !aligned(a_gs, 4) || !aligned(b_alpha, 4))
+    if (!aligned(aq, 16) || !aligned(asf, 8) || !aligned(bq, 16) || !aligned(bsf, 8) ||
+        !aligned(out, 2) || !aligned(a_gs, 4) || !aligned(b_alpha, 4))
         return NVFP4_EINVAL;
+    if (M * (K / 2) >= 0x7FFFFFFF || N * (K / 2) >= 0x7FFFFFFF) return NVFP4_ESHAPE;
     int dv = check_device();
     if (dv) return dv;
     GemmParams p = {};
@@ -179,6 +205,7 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const u
     p.aq = aq;
     p.asf = asf;
     p.M = M;
+    p.a_rows = M;
     p.bq = bq;
     p.bsf = bsf;
     p.N = N;
@@ -216,9 +243,12 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     if (T > 0 && (!aligned(x, 16) || !aligned(y, 16) || !aligned(topk_ids, 4) ||
                   !aligned(topk_weights, 4)))
         return NVFP4_EINVAL;
-    if (!aligned(w13, 4) || !aligned(w2, 4) || !aligned(w13_sf, 8) || !aligned(w2_sf, 8) ||
+    if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_sf, 8) || !aligned(w2_sf, 8) ||
         !aligned(w13_alpha, 4) || !aligned(w2_alpha, 4))
         return NVFP4_EINVAL;
+    if (2 * I * pitch_q(H) >= 0x7FFFFFFF || H * pitch_q(I) >= 0x7FFFFFFF ||
+        T * pitch_q(H) >= 0x7FFFFFFF || T * topk * pitch_q(I) >= 0x7FFFFFFF)
+        return NVFP4_ESHAPE;
     const MoeLayout L = moe_layout(T, H, I, E, topk);
     if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total)
         return NVFP4_EWORKSPACE;
@@ -258,13 +288,14 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     // 2. quantize x
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
     NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
-    NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, xsf, gs1, stream));
+    NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, pitch_q(H), xsf, pitch_sf(H), gs1, stream));
     // 3. L1 grouped GEMM with fused SiLU(gate) * up
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
     GemmParams p1 = {};
     p1.mode = kGemmL1;
     p1.aq = xq;
     p1.asf = xsf;
+    p1.a_rows = T;
     p1.a_gather = sorted_slot;
     p1.topk = (int)topk;
     p1.bq = w13;
@@ -282,13 +313,15 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     NVFP4_TRY(skinny ? launch_skinny(p1, stream) : launch_gemm(p1, stream));
     // 4. requantize act (rows of valid slots only: offsets[E])
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_REQUANT));
-    NVFP4_TRY(launch_quant_rows(act, S, I, offsets + E, amax + 1, aq, asf, gs2, stream));
+    NVFP4_TRY(launch_quant_rows(act, S, I, offsets + E, amax + 1, aq, pitch_q(I), asf, pitch_sf(I), gs2,
+                                stream));
     // 5a. L2 grouped GEMM
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L2));
     GemmParams p2 = {};
     p2.mode = kGemmL2;
     p2.aq = aq;
     p2.asf = asf;
+    p2.a_rows = S;
     p2.bq = w2;
     p2.bsf = w2_sf;
     p2.N = H;

@@ -11,26 +11,32 @@
 // exactly, so the operands are dequantized in registers and fed to
 // v_mfma_f32_32x32x16_f16.
 //
-// Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
-// 128 x 128 quadrant (4 x 4 tiles of v_mfma_f32_32x32x16_f16). The K loop steps 128
-// elements (64 packed bytes) at a time through double-buffered LDS holding the
-// tiles still packed (4 bits per element), so LDS traffic and capacity are a
-// quarter of a bf16 design. Both operands sit in LDS K-contiguous: A rows are
-// K-packed already; B arrives (K/2, N) N-contiguous from HBM and is transposed
-// 4x4 bytes at a time in registers (v_perm) on its way into LDS.
+// Operands. A rows and B rows (one per weight column: the weights in the
+// byte-transposed layout, as the pages' GEMM consumed B column-major) are
+// both K-packed, 64 bytes per 128-element K step, with their E4M3 scales
+// alongside. Tiles move from HBM to LDS by buffer loads that write LDS
+// directly (no staging registers; out-of-range offsets read zeros), four
+// stages deep (36 KB each).
 //
-// K permutation. Inside one 128-element K step, lane half h = lane / 32 reads
-// the 32 bytes (64 elements) [64h, 64h + 64) of its row or column with two
-// 128-bit LDS reads, and MFMA number s (0..7) of the step consumes elements
-// [64h + 8s, 64h + 8s + 8) from both halves. A and B use the same
-// permutation, and each 8-element run lies inside one 16-element scale group,
-// so every k is multiplied with its own partner exactly once. The dequant of
-// substep s + 1 is issued before the MFMAs of substep s so that the VALU work
-// overlaps the matrix cores.
+// LDS layout. A stage holds 256 A rows and 256 B rows of 64 bytes, unpadded;
+// the four 16-byte chunks of a row are XOR-swizzled with bits 2-3 of the row,
+// so that the 16 rows read by a 16-lane group of the fragment loads cover all
+// banks. Scales: 8 bytes per row.
+//
+// Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
+// 128 x 128 quadrant (4 x 4 tiles of 32 x 32 x 16). Lane l serves row / column
+// l % 32 and K half h = l / 32: in a 128-element step it holds elements
+// [64h, 64h + 64) (two 16-byte chunks), and substep s (0..7) feeds the MFMA
+// elements [64h + 8s, +8), inside scale group 4h + s / 2; A and B use the same
+// K permutation, so every k meets its own partner. The dequant of substep s + 1
+// is issued between the MFMAs of substep s.
 //
 // Grouped scheduling. Tiles come from a device-built list (expert, first
 // sorted row, row count); the grid is sized for the worst case and idle
 // work-groups leave at once, so the host never waits for routing counts.
+// Invalid rows and columns of a tile read a valid row instead (their results
+// are never stored); in a partial last K step the scales of the missing
+// groups are zeroed, which zeroes whatever nibbles were read there.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -38,35 +44,51 @@ namespace nvfp4 {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int BM = kGemmBM;
 constexpr int BN = kGemmBN;
 constexpr int KB = 64;                 // packed bytes of K per step (128 elements)
-constexpr int LDT = 80;                // LDS row pitch in bytes (64 data + 16 pad)
 constexpr int NT = 256;                // threads per work-group
+constexpr int NSTAGE = 4;
+constexpr int A_BYTES = BM * KB;       // 16 KB
+constexpr int B_BYTES = BN * KB;
+constexpr int ASF_BYTES = BM * 8;      // 2 KB
+constexpr int BSF_BYTES = BN * 8;
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES + ASF_BYTES + BSF_BYTES;
+constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 144 KB
+constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw buffer, 32-bit data format
 
-struct Smem {
-    uint8_t a[2][BM * LDT];
-    uint8_t b[2][BN * LDT];
-    uint8_t asf[2][BM * 8];
-    uint8_t bsf[2][8 * BN];
-};
+// Work-group barrier for the main loop. __syncthreads() (and any workgroup
+// fence, since the buffer-to-LDS loads count as LDS writes) first drains every
+// outstanding global load, i.e. waits for the stages still in flight. Here the
+// DMA of the stage about to be read is waited for explicitly (vmcnt) before
+// the barrier, and the empty asm statements keep the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
-struct Stage {
-    u32x4 a[4];
-    u32x2 asf;
-    uint32_t b[16];
-    u32x2 bsf;
-};
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
 
 template <int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
-    Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int64_t K = p.K, N = p.N;
-    const int64_t Kh = K / 2, Kg = K / 16;
+    const int64_t Kg = K / 16;                               // real scale groups per row
+    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);      // padded row pitches
     const int ntn = (MODE == kGemmL1) ? (int)((p.I + 127) / 128) : (int)((N + BN - 1) / BN);
     const int tile_idx = blockIdx.x / ntn;
     const int nt = blockIdx.x - tile_idx * ntn;
@@ -85,130 +107,69 @@ void gemm_kernel(GemmParams p) {
         row_count = t.row_count;
     }
 
-    // ---- per-thread load descriptors -------------------------------------
-    // A data: 4 lanes per row, 16 bytes each; rows ar, ar+64, ar+128, ar+192
-    const int ar = tid >> 2, ac = tid & 3;
-    const uint8_t* a_row[4];
-    bool a_ok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int local = ar + 64 * i;
-        a_ok[i] = local < row_count;
-        int64_t src = row_start + (a_ok[i] ? local : 0);
-        if (MODE == kGemmL1) src = p.a_gather[src] / p.topk;
-        a_row[i] = p.aq + src * Kh + 16 * ac;
-    }
-    // A scales: one row per thread
-    const bool asf_ok = tid < row_count;
-    int64_t asf_src = row_start + (asf_ok ? tid : 0);
-    if (MODE == kGemmL1) asf_src = p.a_gather[asf_src] / p.topk;
-    const uint8_t* asf_row = p.asf + asf_src * Kg;
+    // ---- buffer resources and per-lane DMA offsets ---------------------------
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aq, p.a_rows * ldq);
+    const __amdgpu_buffer_rsrc_t rasf = make_rsrc(p.asf, p.a_rows * ldsf);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
+    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldsf, N * ldsf);
 
-    // B column mapping: virtual column vc of the tile -> weight column
-    auto map_col = [&](int vc, bool& ok) -> int64_t {
+    auto a_src = [&](int r) -> int64_t {        // A tensor row of tile row r
+        int64_t src = row_start + (r < row_count ? r : 0);
+        if (MODE == kGemmL1) src = p.a_gather[src] / p.topk;
+        return src;
+    };
+    auto b_src = [&](int vc) -> int64_t {       // weight row (output column) of virtual column vc
         if (MODE == kGemmL1) {
             const int w = vc >> 7, r = vc & 127;
             const int64_t base = (int64_t)nt * 128 + 64 * w + (r & 63);
-            ok = base < p.I;
+            if (base >= p.I) return 0;
             return (r < 64) ? base : p.I + base;
-        } else {
-            const int64_t c = (int64_t)nt * BN + vc;
-            ok = c < N;
-            return c;
         }
+        const int64_t c = (int64_t)nt * BN + vc;
+        return c < N ? c : 0;
     };
-    const int cq = tid & 63, kb = tid >> 6;
-    bool b_ok;
-    const int64_t b_col = map_col(4 * cq, b_ok);
-    const uint8_t* b_base = p.bq + (int64_t)expert * Kh * N + (int64_t)(16 * kb) * N + (b_ok ? b_col : 0);
-    const int g_row = tid >> 5, vc8 = 8 * (tid & 31);
-    bool bsf_ok;
-    const int64_t bsf_col = map_col(vc8, bsf_ok);
-    const uint8_t* bsf_base = p.bsf + (int64_t)expert * Kg * N + (int64_t)g_row * N + (bsf_ok ? bsf_col : 0);
+    // data: wave w, instruction t (0..3) fills LDS slots (4w + t) * 64 + lane of
+    // 16 bytes: row (4w + t) * 16 + lane / 4, physical chunk lane & 3
+    uint32_t a_off[4], b_off[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int row = (4 * wave + t) * 16 + (lane >> 2);
+        const int chunk = swz(row, lane & 3);
+        a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
+        b_off[t] = (uint32_t)(b_src(row) * ldq + 16 * chunk);
+    }
+    // scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 + lane:
+    // row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the step's 8
+    uint32_t asf_off[2], bsf_off[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int row = (2 * wave + t) * 32 + (lane >> 1);
+        asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
+        bsf_off[t] = (uint32_t)(b_src(row) * ldsf + 4 * (lane & 1));
+    }
 
-    const bool a_vec16 = (Kh % 16) == 0;
-    const bool asf_vec8 = (Kg % 8) == 0;
-    const int nk = (int)((K + 127) / 128);
-
-    auto load_stage = [&](int ks, Stage& st) {
-        const int64_t kb0 = (int64_t)ks * KB;
+    const int nk = (int)(ldq / KB);
+    auto issue_stage = [&](int ks) {
+        uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
+        const uint32_t kd = (uint32_t)ks * KB, ksf = (uint32_t)ks * 8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            const int64_t off = kb0 + 16 * ac;
-            if (a_ok[i] && off < Kh) {
-                if (a_vec16) {
-                    v = *reinterpret_cast<const u32x4*>(a_row[i] + kb0);
-                } else {
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(a_row[i] + kb0);
-                    v[0] = lo[0];
-                    v[1] = lo[1];
-                    if (off + 8 < Kh) {
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(a_row[i] + kb0 + 8);
-                        v[2] = hi[0];
-                        v[3] = hi[1];
-                    }
-                }
-            }
-            st.a[i] = v;
-        }
-        {
-            u32x2 v = {0u, 0u};
-            const int64_t g0 = (int64_t)ks * 8;
-            if (asf_ok) {
-                if (asf_vec8 && g0 + 8 <= Kg) {
-                    v = *reinterpret_cast<const u32x2*>(asf_row + g0);
-                } else {
-                    for (int g = 0; g < 8; ++g)
-                        if (g0 + g < Kg) v[g >> 2] |= (uint32_t)asf_row[g0 + g] << (8 * (g & 3));
-                }
-            }
-            st.asf = v;
-        }
-        const uint8_t* bp = b_base + kb0 * N;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t kh = kb0 + 16 * kb + r;
-            st.b[r] = (b_ok && kh < Kh) ? *reinterpret_cast<const uint32_t*>(bp + (int64_t)r * N) : 0u;
-        }
-        {
-            u32x2 v = {0u, 0u};
-            if (bsf_ok && (int64_t)ks * 8 + g_row < Kg)
-                v = *reinterpret_cast<const u32x2*>(bsf_base + (int64_t)ks * 8 * N);
-            st.bsf = v;
-        }
-    };
-
-    auto store_stage = [&](int buf, const Stage& st) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(&sm.a[buf][(ar + 64 * i) * LDT + 16 * ac]) = st.a[i];
-        *reinterpret_cast<u32x2*>(&sm.asf[buf][tid * 8]) = st.asf;
-        uint32_t col[4][4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const uint32_t r4[4] = {st.b[4 * jb], st.b[4 * jb + 1], st.b[4 * jb + 2], st.b[4 * jb + 3]};
-            uint32_t c4[4];
-            transpose4x4(r4, c4);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) col[c][jb] = c4[c];
+        for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
+                                                     16, a_off[t], kd, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
+                                                     16, b_off[t], kd, 0, 0);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            u32x4 v = {col[c][0], col[c][1], col[c][2], col[c][3]};
-            *reinterpret_cast<u32x4*>(&sm.b[buf][(4 * cq + c) * LDT + 16 * kb]) = v;
+        for (int t = 0; t < 2; ++t) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + t) * 256), 4, asf_off[t], ksf, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (2 * wave + t) * 256), 4,
+                bsf_off[t], ksf, 0, 0);
         }
-        *reinterpret_cast<u32x2*>(&sm.bsf[buf][g_row * BN + vc8]) = st.bsf;
     };
 
     // ---- main loop ---------------------------------------------------------
-    // Wave (wm, wn) owns rows [128 wm, +128) and virtual columns [128 wn, +128)
-    // of the tile as 4 x 4 blocks of the 32 x 32 x 16 MFMA. Lane l serves row /
-    // column (l & 31) of a block and K half h = l >> 5: inside a 128-element K
-    // step it holds elements [64h, 64h + 64) (32 bytes, two 128-bit LDS reads),
-    // and substep s (0..7) feeds the MFMA elements [64h + 8s, 64h + 8s + 8),
-    // which lie in scale group 4h + s/2.
-    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int l32 = lane & 31, h = lane >> 5;
 
@@ -220,37 +181,52 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    Stage st;
-    load_stage(0, st);
-    store_stage(0, st);
-    __syncthreads();
-
-    for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        const bool more = ks + 1 < nk;
-        if (more) load_stage(ks + 1, st);
-
-        u32x4 fa[4][2], fb[4][2];
-        uint32_t sa[4], sb[4];
+    u32x4 fa[4][2], fb[4][2];
+    uint32_t sa[4], sb[4];
+    auto read_frags = [&](int ks) {
+        const uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
+        const uint8_t* sA = base;
+        const uint8_t* sB = base + A_BYTES;
+        const uint8_t* sAsf = base + A_BYTES + B_BYTES;
+        const uint8_t* sBsf = sAsf + ASF_BYTES;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = wm * 128 + 32 * i + l32;
-            const uint8_t* pa = &sm.a[buf][row * LDT + 32 * h];
-            fa[i][0] = *reinterpret_cast<const u32x4*>(pa);
-            fa[i][1] = *reinterpret_cast<const u32x4*>(pa + 16);
-            sa[i] = *reinterpret_cast<const uint32_t*>(&sm.asf[buf][row * 8 + 4 * h]);
+            fa[i][0] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h));
+            fa[i][1] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h + 1));
+            sa[i] = *reinterpret_cast<const uint32_t*>(sAsf + row * 8 + 4 * h);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int vc = wn * 128 + 32 * j + l32;
-            const uint8_t* pb = &sm.b[buf][vc * LDT + 32 * h];
-            fb[j][0] = *reinterpret_cast<const u32x4*>(pb);
-            fb[j][1] = *reinterpret_cast<const u32x4*>(pb + 16);
-            const uint8_t* ps = &sm.bsf[buf][(4 * h) * BN + vc];
-            sb[j] = (uint32_t)ps[0] | ((uint32_t)ps[BN] << 8) | ((uint32_t)ps[2 * BN] << 16) |
-                    ((uint32_t)ps[3 * BN] << 24);
+            fb[j][0] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h));
+            fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
+            sb[j] = *reinterpret_cast<const uint32_t*>(sBsf + vc * 8 + 4 * h);
         }
+        // partial last step: scale groups beyond K read zero scales
+        const int64_t g0 = (int64_t)ks * 8 + 4 * h;
+        if (g0 + 4 > Kg) {
+            uint32_t mask = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (g0 + b < Kg) mask |= 0xFFu << (8 * b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sa[i] &= mask;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sb[j] &= mask;
+        }
+    };
 
+    // Pipeline: stages ks+1..ks+3 are in flight while step ks computes; the
+    // barrier before the fragment reads of step ks+1 (in substep 7) makes the
+    // other waves' DMA of that stage visible and frees buffer (ks-1) % 4.
+    for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    read_frags(0);
+
+    for (int ks = 0; ks < nk; ++ks) {
+        if (ks + NSTAGE - 1 < nk) issue_stage(ks + NSTAGE - 1);
         half8_t ha[2][4], hb[2][4];
         auto deq = [&](int s, half8_t (&xa)[4], half8_t (&xb)[4]) {
 #pragma unroll
@@ -264,17 +240,31 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             if (s < 7) deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
+            if (s == 7 && ks + 1 < nk) {
+                // this wave's DMA of stage ks+1 is done when at most the stages
+                // issued after it (up to two, 12 loads each) are outstanding
+                if (ks + NSTAGE - 1 < nk) __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24)
+                else if (ks + NSTAGE - 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
+                else __builtin_amdgcn_s_waitcnt(0x0F70);                             // vmcnt(0)
+                lds_barrier();
+                read_frags(ks + 1);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[s & 1][i], hb[s & 1][j],
                                                                         acc[i][j], 0, 0, 0);
+            if (s < 7) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // four VALU
+                }
+            }
         }
-
-        if (more) store_stage(buf ^ 1, st);
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- epilogue ------------------------------------------------------------
     // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
@@ -349,21 +339,22 @@ hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     const int64_t mt = (MODE == kGemmDense) ? (p.M + BM - 1) / BM : p.max_tiles;
     const int64_t grid = mt * ntn;
     if (grid <= 0) return hipSuccess;
-    const size_t lds = sizeof(Smem);
     static bool configured = false;
     if (!configured) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
         configured = true;
     }
-    gemm_kernel<MODE><<<(unsigned)grid, NT, lds, s>>>(p);
+    gemm_kernel<MODE><<<(unsigned)grid, NT, LDS_BYTES, s>>>(p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
+    // 32-bit buffer offsets: every operand must stay below 2 GiB
+    if (p.a_rows * pitch_q(p.K) >= 0x7FFFFFFF || p.N * pitch_q(p.K) >= 0x7FFFFFFF) return hipErrorInvalidValue;
     switch (p.mode) {
         case kGemmDense: return launch_mode<kGemmDense>(p, s);
         case kGemmL1: return launch_mode<kGemmL1>(p, s);

@@ -34,9 +34,20 @@ hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, u
 
 // Row-block quantization of x (M, K) with amax taken from *amax_slot. Rows at or
 // beyond *m_dev (when m_dev is not null) are left untouched. gs_out receives gs.
+// Output rows are ldq bytes (q) and ldsf bytes (sf) apart.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
-                             const uint32_t* amax_slot, uint8_t* q, uint8_t* sf, float* gs_out,
-                             hipStream_t s);
+                             const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
+                             int64_t ldsf, float* gs_out, hipStream_t s);
+
+// Row pitches of the GEMM operand layout: packed data padded to whole
+// 128-element K steps, scales to whole 8-byte steps.
+__host__ __device__ inline int64_t pitch_q(int64_t K) { return (K / 2 + 63) / 64 * 64; }
+__host__ __device__ inline int64_t pitch_sf(int64_t K) { return (K / 16 + 7) / 8 * 8; }
+
+// Byte transpose of E matrices (R, C) -> (C, ldo) with zero padding of the
+// rows from R to ldo bytes.
+hipError_t launch_transpose_bytes(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
+                                  int64_t ldo, hipStream_t s);
 
 // Column-block quantization of E weight matrices (E, K, N) with per-matrix amax.
 hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
@@ -58,13 +69,15 @@ enum GemmMode { kGemmDense = 0, kGemmL1 = 1, kGemmL2 = 2 };
 
 struct GemmParams {
     int mode;
-    // A: rows of quantized activations
+    // A: rows of quantized activations, pitches pitch_q(K) / pitch_sf(K)
     const uint8_t* aq;
     const uint8_t* asf;
     int64_t M;                 // dense: rows of A
+    int64_t a_rows;            // rows in the A tensor (bounds of the buffer loads)
     const int32_t* a_gather;   // L1: sorted row -> slot index; token = slot / topk
     int topk;
-    // B: per-expert K-packed weights
+    // B: per-expert weights, one K-packed row per output column (N rows of
+    // pitch_q(K) bytes, scales N rows of pitch_sf(K) bytes)
     const uint8_t* bq;
     const uint8_t* bsf;
     int64_t N;                 // columns of B

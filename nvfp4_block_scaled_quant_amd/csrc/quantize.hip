@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
 // One thread per 16-element block of a row-major (M, K) bf16 matrix.
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ m_dev,
-    const uint32_t* __restrict__ amax_slot, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
-    float* __restrict__ gs_out) {
+    const uint32_t* __restrict__ amax_slot, uint8_t* __restrict__ q, int64_t ldq,
+    uint8_t* __restrict__ sf, int64_t ldsf, float* __restrict__ gs_out) {
     const float amax = __uint_as_float(*amax_slot);
     const QuantScales qs = make_scales(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = qs.gs;
@@ -78,8 +78,31 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         u32x2 out;
         out[0] = packed[0];
         out[1] = packed[1];
-        *reinterpret_cast<u32x2*>(q + b * 8) = out;
-        sf[b] = (uint8_t)code;
+        const int64_t r = b / groups, g = b - r * groups;
+        *reinterpret_cast<u32x2*>(q + r * ldq + g * 8) = out;
+        sf[r * ldsf + g] = (uint8_t)code;
+    }
+}
+
+// Byte transpose of E matrices (R, C) -> (C, ldo), rows zero-padded from R to
+// ldo bytes, through a 64 x 64 LDS tile.
+__global__ __launch_bounds__(kThreads) void transpose_bytes_kernel(
+    const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out, int64_t ldo) {
+    __shared__ uint8_t tile[64][65];
+    const int64_t e = blockIdx.z;
+    const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+    const uint8_t* src = in + e * R * C;
+    uint8_t* dst = out + e * C * ldo;
+    for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
+        const int rr = i >> 6, cc = i & 63;
+        const int64_t r = r0 + rr, c = c0 + cc;
+        tile[rr][cc] = (r < R && c < C) ? src[r * C + c] : (uint8_t)0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
+        const int cc = i >> 6, rr = i & 63;
+        const int64_t r = r0 + rr, c = c0 + cc;
+        if (c < C && r < ldo) dst[c * ldo + r] = tile[rr][cc];
     }
 }
 
@@ -147,10 +170,19 @@ hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, u
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
-                             const uint32_t* amax_slot, uint8_t* q, uint8_t* sf, float* gs_out,
-                             hipStream_t s) {
+                             const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
+                             int64_t ldsf, float* gs_out, hipStream_t s) {
     const int g = grid_for(M * (K / 16), 1 << 20);
-    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, q, sf, gs_out);
+    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, q, ldq, sf, ldsf, gs_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bytes(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
+                                  int64_t ldo, hipStream_t s) {
+    if (E <= 0 || C <= 0) return hipSuccess;
+    // rows of the output beyond R (padding) are covered by extra row tiles
+    const int64_t rt = (ldo + 63) / 64, ct = (C + 63) / 64;
+    transpose_bytes_kernel<<<dim3((unsigned)ct, (unsigned)rt, (unsigned)E), kThreads, 0, s>>>(in, R, C, out, ldo);
     return hipGetLastError();
 }
 

@@ -130,11 +130,22 @@ def run_oracle_layer(L, keep=True, pool=None):
                        L["w2q"], L["w2sf"], L["w2a"], keep=keep, pool=pool)
 
 
-def run_gpu_layer(nv, L, repeat=1):
-    """Run nvfp4_moe_forward; return y bits and the workspace intermediates."""
+def gpu_packed_weights(nv, L):
+    """Upload the canonical weights of L and prepack them on the device."""
+    from conftest import to_dev
+    w13, w13_sf = nv.prepack_weights(to_dev(L["w13q"]), to_dev(L["w13sf"]))
+    w2, w2_sf = nv.prepack_weights(to_dev(L["w2q"]), to_dev(L["w2sf"]))
+    return dict(w13=w13, w13_sf=w13_sf, w13a=to_dev(L["w13a"]),
+                w2=w2, w2_sf=w2_sf, w2a=to_dev(L["w2a"]))
+
+
+def run_gpu_layer(nv, L, repeat=1, packed=None):
+    """Run nvfp4_moe_forward; return y bits and the workspace intermediates
+    (quantized operands cut to their unpadded widths)."""
     import torch
     from conftest import to_dev, to_host
-    d = {k: to_dev(v) for k, v in L.items()}
+    d = {k: to_dev(L[k]) for k in ("x", "ids", "wts")}
+    pw = gpu_packed_weights(nv, L) if packed is None else packed
     T, H = L["x"].shape
     k = L["ids"].shape[1]
     E = L["w13q"].shape[0]
@@ -143,25 +154,27 @@ def run_gpu_layer(nv, L, repeat=1):
     ws = torch.empty((nws,), dtype=torch.uint8, device="cuda")
     ys = []
     for _ in range(repeat):
-        y = nv.moe_forward(d["x"], d["ids"], d["wts"], d["w13q"], d["w13sf"], d["w13a"],
-                           d["w2q"], d["w2sf"], d["w2a"], workspace=ws)
+        y = nv.moe_forward(d["x"], d["ids"], d["wts"], pw["w13"], pw["w13_sf"], pw["w13a"],
+                           pw["w2"], pw["w2_sf"], pw["w2a"], workspace=ws)
         ys.append(to_host(y))
     torch.cuda.synchronize()
     lay = nv.moe_workspace_layout(T, H, I, E, k)
     wsh = ws.cpu().numpy()
     S = T * k
+    ldq_h, ldsf_h = nv.operand_pitches(H)
+    ldq_i, ldsf_i = nv.operand_pitches(I)
 
     def view(name, dtype, count):
         o = lay[name]
         return wsh[o:o + count * np.dtype(dtype).itemsize].view(dtype)
 
     out = {"y": ys[-1], "ys": ys,
-           "xq": view("xq", np.uint8, T * H // 2).reshape(T, H // 2),
-           "xsf": view("xsf", np.uint8, T * H // 16).reshape(T, H // 16),
+           "xq": view("xq", np.uint8, T * ldq_h).reshape(T, ldq_h)[:, :H // 2],
+           "xsf": view("xsf", np.uint8, T * ldsf_h).reshape(T, ldsf_h)[:, :H // 16],
            "gs1": view("gs1", np.float32, 1)[0], "gs2": view("gs2", np.float32, 1)[0],
            "counts": view("counts", np.int32, E), "offsets": view("offsets", np.int32, E + 1),
            "sorted_slot": view("sorted_slot", np.int32, S), "slot_row": view("slot_row", np.int32, S),
            "act": view("act", np.uint16, S * I).reshape(S, I),
-           "aq": view("aq", np.uint8, S * I // 2).reshape(S, I // 2),
-           "asf": view("asf", np.uint8, S * I // 16).reshape(S, I // 16)}
+           "aq": view("aq", np.uint8, S * ldq_i).reshape(S, ldq_i)[:, :I // 2],
+           "asf": view("asf", np.uint8, S * ldsf_i).reshape(S, ldsf_i)[:, :I // 16]}
     return out

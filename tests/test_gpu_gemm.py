@@ -22,13 +22,16 @@ def _operands(M, N, K, seed, a_std=3.0):
 
 
 def _run(nv, aq, asf, ags, bq, bsf, balpha):
-    out = nv.gemm(to_dev(aq), to_dev(asf), to_dev(np.array([ags], np.float32)), to_dev(bq),
-                  to_dev(bsf), to_dev(np.array([balpha], np.float32)))
+    # canonical B (K/2, N) -> the packed (N, K/2) layout, on the device
+    bq_t, bsf_t = nv.prepack_weights(to_dev(bq)[None], to_dev(bsf)[None])
+    out = nv.gemm(to_dev(aq), to_dev(asf), to_dev(np.array([ags], np.float32)), bq_t[0],
+                  bsf_t[0], to_dev(np.array([balpha], np.float32)))
     return to_host(out)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (3, 32, 48), (17, 272, 144), (256, 256, 256),
-                                   (300, 512, 1024), (257, 48, 7168), (64, 6144, 128)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 32, 384), (17, 272, 640), (256, 256, 256),
+                                   (300, 512, 1024), (257, 48, 7168), (64, 6144, 128),
+                                   (513, 784, 896)])
 def test_gemm_random(nv, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     out = _run(nv, *ops)
@@ -55,7 +58,7 @@ def test_gemm_constant_scale_bit_exact(nv):
     # equal the correctly rounded oracle bit for bit (src commit log,
     # constant-scale test)
     rng = np.random.default_rng(1)
-    M, N, K = 40, 64, 64
+    M, N, K = 40, 64, 128
     aq = rng.integers(0, 256, (M, K // 2)).astype(np.uint8)
     bq = rng.integers(0, 256, (K // 2, N)).astype(np.uint8)
     asf = np.full((M, K // 16), 0x38, np.uint8)

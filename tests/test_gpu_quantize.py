@@ -112,3 +112,18 @@ def test_quantize_weights_full_expert(nv):
         assert alpha[0].view(np.uint32) == np.float32(ra).view(np.uint32)
         assert (sf[0] == rsf).all()
         assert (q[0] == rq).all()
+
+
+@pytest.mark.parametrize("E,K,N", [(1, 16, 16), (3, 272, 40), (2, 256, 200), (1, 7168, 96),
+                                   (4, 400, 130)])
+def test_prepack_weights_is_a_padded_transpose(nv, E, K, N):
+    # pure data movement: byte-exact against a NumPy transpose, padding zero
+    rng = np.random.default_rng(E + K + N)
+    q = rng.integers(0, 256, (E, K // 2, N)).astype(np.uint8)
+    sf = rng.integers(0, 256, (E, K // 16, N)).astype(np.uint8)
+    q_t, sf_t = (to_host(t) for t in nv.prepack_weights(to_dev(q), to_dev(sf)))
+    ldq, ldsf = nv.operand_pitches(K)
+    assert q_t.shape == (E, N, ldq) and sf_t.shape == (E, N, ldsf)
+    assert (q_t[:, :, :K // 2] == q.transpose(0, 2, 1)).all()
+    assert (sf_t[:, :, :K // 16] == sf.transpose(0, 2, 1)).all()
+    assert (q_t[:, :, K // 2:] == 0).all() and (sf_t[:, :, K // 16:] == 0).all()

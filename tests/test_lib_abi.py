@@ -26,7 +26,8 @@ def nv():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("nvfp4_quantize", "nvfp4_moe_forward", "nvfp4_gemm", "nvfp4_strerror",
-                 "nvfp4_quantize_weights", "nvfp4_moe_workspace"):
+                 "nvfp4_quantize_weights", "nvfp4_moe_workspace", "nvfp4_prepack_weights",
+                 "nvfp4_operand_pitches"):
         assert must in names
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (1, 0)
+    assert nv.version() == (2, 0)
     for code in range(6):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
@@ -84,11 +85,36 @@ def test_gemm_argument_errors(nv):
     f = lib(nv).nvfp4_gemm
     args = [p(A16)] * 6
     assert f(*args, 4, 16, 24, p(A16), None) == 2       # K % 16
-    assert f(*args, 4, 24, 32, p(A16), None) == 2       # N % 16
-    assert f(*args, -4, 16, 32, p(A16), None) == 1
-    assert f(*args, 0, 16, 32, p(A16), None) == 0       # M == 0: nothing to do
+    assert f(*args, 4, 16, 64, p(A16), None) == 2       # K % 128
+    assert f(*args, 4, 24, 128, p(A16), None) == 2      # N % 16
+    assert f(*args, -4, 16, 128, p(A16), None) == 1
+    assert f(*args, 0, 16, 128, p(A16), None) == 0      # M == 0: nothing to do
     bad = [p(A16)] * 5 + [p(0)]
-    assert f(*bad, 4, 16, 32, p(A16), None) == 1
+    assert f(*bad, 4, 16, 128, p(A16), None) == 1
+    mis = [p(A16)] * 3 + [p(A16 + 8)] + [p(A16)] * 2   # bq not 16-byte aligned
+    assert f(*mis, 4, 16, 128, p(A16), None) == 1
+    assert f(*args, 1 << 20, 16, 1 << 13, p(A16), None) == 2   # A beyond 32-bit offsets
+
+
+def test_operand_pitches(nv):
+    for K, want in [(16, (64, 8)), (128, (64, 8)), (144, (128, 16)), (272, (192, 24)),
+                    (7168, (3584, 448)), (3072, (1536, 192)), (400, (256, 32))]:
+        assert nv.operand_pitches(K) == want
+    ldq, ldsf = ctypes.c_int64(), ctypes.c_int64()
+    f = lib(nv).nvfp4_operand_pitches
+    assert f(24, ctypes.byref(ldq), ctypes.byref(ldsf)) == 2
+    assert f(0, ctypes.byref(ldq), ctypes.byref(ldsf)) == 1
+    assert f(32, None, ctypes.byref(ldsf)) == 1
+
+
+def test_prepack_argument_errors(nv):
+    f = lib(nv).nvfp4_prepack_weights
+    assert f(p(A16), p(A16), 2, 24, 16, p(A16), p(A16), None) == 2        # K % 16
+    assert f(p(A16), p(A16), -1, 32, 16, p(A16), p(A16), None) == 1
+    assert f(p(A16), p(A16), 2, 32, 0, p(A16), p(A16), None) == 1
+    assert f(p(0), p(A16), 2, 32, 16, p(A16), p(A16), None) == 1
+    assert f(p(A16), p(A16), 2, 32, 16, p(A16 + 4), p(A16), None) == 1    # w_t alignment
+    assert f(p(0), p(0), 0, 32, 16, p(0), p(0), None) == 0                 # E == 0: nothing
 
 
 def test_moe_argument_errors(nv):
@@ -118,9 +144,11 @@ def test_moe_workspace_layout_is_consistent(nv):
         total = nv.moe_workspace_size(*shape)
         lay = nv.moe_workspace_layout(*shape)
         S = T * k
-        ends = {"xq": T * H // 2, "xsf": T * H // 16, "gs1": 4, "gs2": 4, "counts": 4 * E,
+        qh, sh = nv.operand_pitches(H)
+        qi, si = nv.operand_pitches(I)
+        ends = {"xq": T * qh, "xsf": T * sh, "gs1": 4, "gs2": 4, "counts": 4 * E,
                 "offsets": 4 * (E + 1), "sorted_slot": 4 * S, "slot_row": 4 * S,
-                "act": 2 * S * I, "aq": S * I // 2, "asf": S * I // 16, "o2": 4 * S * H}
+                "act": 2 * S * I, "aq": S * qi, "asf": S * si, "o2": 4 * S * H}
         spans = sorted((lay[n], lay[n] + ends[n]) for n in ends)
         for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
             assert a1 <= b0
