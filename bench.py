@@ -69,12 +69,12 @@ def make_weights(nv, cfg):
     import torch
     import workloads as W
     E, H, I = cfg.E, cfg.H, cfg.I
-    qh, sh = nv.operand_pitches(H)
-    qi, si = nv.operand_pitches(I)
-    w13 = torch.empty((E, 2 * I, qh), dtype=torch.uint8, device="cuda")
-    w13sf = torch.empty((E, 2 * I, sh), dtype=torch.uint8, device="cuda")
-    w2 = torch.empty((E, H, qi), dtype=torch.uint8, device="cuda")
-    w2sf = torch.empty((E, H, si), dtype=torch.uint8, device="cuda")
+    s13, s13f = nv.packed_shapes(E, H, 2 * I)
+    s2, s2f = nv.packed_shapes(E, I, H)
+    w13 = torch.empty(s13, dtype=torch.uint8, device="cuda")
+    w13sf = torch.empty(s13f, dtype=torch.uint8, device="cuda")
+    w2 = torch.empty(s2, dtype=torch.uint8, device="cuda")
+    w2sf = torch.empty(s2f, dtype=torch.uint8, device="cuda")
     w13a = torch.empty((E,), dtype=torch.float32, device="cuda")
     w2a = torch.empty((E,), dtype=torch.float32, device="cuda")
     for e in range(E):

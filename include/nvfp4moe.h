@@ -25,15 +25,25 @@
  *   weights               holds W[2kh][n] (low) and W[2kh+1][n] (high)
  *                w_sf     (E, K/16, N) E4M3 bytes
  *                w_alpha  (E) float32 weight global scales (dequant direction)
- *   packed       w_t      (E, N, pitch_q(K)) bytes: row n of matrix e holds
+ *   packed       w_t      E * N * pitch_q(K) bytes: row n of matrix e holds
  *   weights               column n of W[e], packed along K like an A row
  *                         (byte kh = W[2kh][n] | W[2kh+1][n] << 4), zero-padded
- *                w_sf_t   (E, N, pitch_sf(K)) E4M3 bytes, zero-padded
+ *                         to pitch_q(K) bytes; rows are stored in blocks of 16
+ *                         and inside a block by 128-element K step: byte kh of
+ *                         row n is at
+ *                           e * N * pitch_q(K) + (n / 16) * 16 * pitch_q(K)
+ *                           + (kh / 64) * 1024 + (n % 16) * 64 + kh % 64
+ *                w_sf_t   E * N * pitch_sf(K) E4M3 bytes, zero-padded, the same
+ *                         blocking with 8-byte steps: scale g of row n is at
+ *                           e * N * pitch_sf(K) + (n / 16) * 16 * pitch_sf(K)
+ *                           + (g / 8) * 128 + (n % 16) * 8 + g % 8
  *   pitch_q(K)  = K/2 rounded up to a multiple of 64 bytes (a 128-element step)
  *   pitch_sf(K) = K/16 rounded up to a multiple of 8 bytes
  *   The packed weights are the canonical ones with every matrix byte-transposed
- *   (the pages' GEMM took its weight operand column-major); they are made once,
- *   at load time, by nvfp4_prepack_weights and are what the GEMMs read.
+ *   (the pages' GEMM took its weight operand column-major) and blocked so that
+ *   one K step of 16 rows, the unit a matrix-core operand load covers, is one
+ *   contiguous kilobyte. They are made once, at load time, by
+ *   nvfp4_prepack_weights and are what the GEMMs read. N % 16 == 0.
  *   w13 is the plain concatenation [gate; up] along N: columns [0, I) are the
  *   gate projection, [I, 2I) the up projection (rows [0, I) / [I, 2I) packed).
  *
@@ -125,13 +135,13 @@ int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf);
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_prepack_weights - canonical (K-packed, N fastest) quantized weights to
- * the packed layout the GEMMs read (one byte transpose per matrix, padding
- * bytes written as zero). A pure data movement, no arithmetic.
+ * the packed layout the GEMMs read (a blocked byte transpose per matrix,
+ * padding bytes written as zero). A pure data movement, no arithmetic.
  *
  *   w (E, K/2, N), w_sf (E, K/16, N): canonical bytes (nvfp4_quantize_weights)
- *   w_t (E, N, pitch_q(K)), w_sf_t (E, N, pitch_sf(K)): packed out, separate
- *   buffers (no in-place), w_t 16-byte and w_sf_t 8-byte aligned.
- *   K % 16 == 0, E <= 65535. E == 0 is valid and enqueues nothing.
+ *   w_t (E * N * pitch_q(K) bytes), w_sf_t (E * N * pitch_sf(K) bytes): packed
+ *   out, separate buffers (no in-place), w_t 16-byte and w_sf_t 8-byte aligned.
+ *   K % 16 == 0, N % 16 == 0, E <= 65535. E == 0 is valid and enqueues nothing.
  * ------------------------------------------------------------------------ */
 int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int64_t K, int64_t N,
                           uint8_t* w_t, uint8_t* w_sf_t, hipStream_t stream);
@@ -145,9 +155,9 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
  *   aq (M, K/2), asf (M, K/16): the quantized activation (nvfp4_quantize),
  *           aq 16-byte and asf 8-byte aligned
  *   a_gs    one float32, the activation's global scale
- *   bq (N, K/2), bsf (N, K/16): one packed weight matrix (nvfp4_prepack_weights
- *           with E = 1; for K % 128 == 0 the pitches are exactly K/2 and K/16),
- *           bq 16-byte and bsf 8-byte aligned
+ *   bq (N * K/2 bytes), bsf (N * K/16 bytes): one packed weight matrix
+ *           (nvfp4_prepack_weights with E = 1; for K % 128 == 0 the pitches
+ *           are exactly K/2 and K/16), bq 16-byte and bsf 8-byte aligned
  *   b_alpha one float32
  *   out (M, N) bf16
  * Products of dequantized elements are exact; the sum is float32; the alpha
@@ -173,8 +183,8 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *   x             (T, H) bf16
  *   topk_ids      (T, topk) int32
  *   topk_weights  (T, topk) float32, used as given (no renormalization)
- *   w13 (E, 2I, pitch_q(H)), w13_sf (E, 2I, pitch_sf(H)), w13_alpha (E)
- *   w2  (E, H, pitch_q(I)),  w2_sf  (E, H, pitch_sf(I)),  w2_alpha  (E)
+ *   w13 (E * 2I * pitch_q(H) bytes), w13_sf (E * 2I * pitch_sf(H)), w13_alpha (E)
+ *   w2  (E * H * pitch_q(I) bytes),  w2_sf  (E * H * pitch_sf(I)),  w2_alpha  (E)
  *                 packed weights (nvfp4_prepack_weights of the canonical
  *                 (E, H/2, 2I) and (E, I/2, H) tensors); w13, w2 16-byte and
  *                 the scale tensors 8-byte aligned

@@ -7,6 +7,7 @@ mirror the C ABI in include/nvfp4moe.h:
     quantize(x)                      -> (q, sf, gs)
     quantize_weights(w)              -> (q, sf, alpha)    canonical weight layout
     operand_pitches(K)               -> (ldq, ldsf)
+    packed_shapes(E, K, N)           -> shapes of the packed weight tensors
     prepack_weights(q, sf)           -> (q_t, sf_t)       packed layout the GEMMs read
     gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
     moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
@@ -141,35 +142,48 @@ def operand_pitches(K):
     return ldq.value, ldsf.value
 
 
+def packed_shapes(E, K, N):
+    """Shapes of the packed weight tensors of E matrices (K, N): 16-row blocks
+    of one 128-element K step each, (E, N/16, steps, 16, 64) data bytes and
+    (E, N/16, steps, 16, 8) scale bytes, steps = pitch_q(K) / 64."""
+    ldq, ldsf = operand_pitches(K)
+    if N % 16:
+        raise ValueError("packed weights need N % 16 == 0")
+    return (E, N // 16, ldq // 64, 16, 64), (E, N // 16, ldsf // 8, 16, 8)
+
+
 def prepack_weights(q, sf):
     """Canonical quantized weights q (E, K/2, N), sf (E, K/16, N) -> the packed
-    layout (E, N, pitch_q(K)), (E, N, pitch_sf(K)) that gemm and moe_forward read."""
+    layout that gemm and moe_forward read (see packed_shapes)."""
     _need(q, torch.uint8, "q", 3)
     _need(sf, torch.uint8, "sf", 3)
     E, Kh, N = q.shape
     K = 2 * Kh
     if sf.shape != (E, K // 16, N):
         raise ValueError("prepack_weights: q and sf shapes do not match")
-    ldq, ldsf = operand_pitches(K)
-    q_t = torch.empty((E, N, ldq), dtype=torch.uint8, device=q.device)
-    sf_t = torch.empty((E, N, ldsf), dtype=torch.uint8, device=q.device)
+    shq, shs = packed_shapes(E, K, N)
+    q_t = torch.empty(shq, dtype=torch.uint8, device=q.device)
+    sf_t = torch.empty(shs, dtype=torch.uint8, device=q.device)
     _check(_lib.nvfp4_prepack_weights(_ptr(q), _ptr(sf), E, K, N, _ptr(q_t), _ptr(sf_t),
                                       _stream()), "nvfp4_prepack_weights")
     return q_t, sf_t
 
 
 def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
-    """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times the
-    packed weight bq (N, K/2) + bsf (N, K/16) -> bf16 (M, N). K % 128 == 0."""
+    """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times one
+    packed weight matrix bq (N/16, K/128, 16, 64) + bsf (N/16, K/128, 16, 8)
+    -> bf16 (M, N). K % 128 == 0."""
     for t, n, d in ((aq, "aq", torch.uint8), (asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
                     (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
                     (b_alpha, "b_alpha", torch.float32)):
         _need(t, d, n)
+    if aq.dim() != 2 or bq.dim() != 4:
+        raise ValueError("gemm: aq must be (M, K/2) and bq (N/16, K/128, 16, 64)")
     M = aq.shape[0]
     K = aq.shape[1] * 2
-    N = bq.shape[0]
-    if (aq.dim() != 2 or bq.dim() != 2 or bq.shape[1] * 2 != K or asf.shape != (M, K // 16)
-            or bsf.shape != (N, K // 16)):
+    N = bq.shape[0] * 16
+    if (K % 128 or tuple(bq.shape) != (N // 16, K // 128, 16, 64) or asf.shape != (M, K // 16)
+            or tuple(bsf.shape) != (N // 16, K // 128, 16, 8)):
         raise ValueError("operand shapes do not match")
     out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device) if out is None else out
     _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),
@@ -193,28 +207,27 @@ def moe_workspace_layout(T, H, I, E, topk):
 def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
                 y=None, workspace=None, stage_events=None):
     """The five-stage NVFP4 expert layer. Weights in the packed layout
-    (prepack_weights): w13 (E, 2I, pitch_q(H)), w13_sf (E, 2I, pitch_sf(H)),
-    w2 (E, H, pitch_q(I)), w2_sf (E, H, pitch_sf(I)).
+    (prepack_weights of the canonical (E, H/2, 2I) and (E, I/2, H) tensors).
 
     stage_events: None or a StageEvents; returns y (T, H) bf16.
     """
     _need(x, torch.bfloat16, "x", 2)
     _need(topk_ids, torch.int32, "topk_ids", 2)
     _need(topk_weights, torch.float32, "topk_weights", 2)
-    for t, n, d in ((w13, "w13", 3), (w13_sf, "w13_sf", 3), (w2, "w2", 3), (w2_sf, "w2_sf", 3)):
-        _need(t, torch.uint8, n, d)
+    for t, n in ((w13, "w13"), (w13_sf, "w13_sf"), (w2, "w2"), (w2_sf, "w2_sf")):
+        _need(t, torch.uint8, n, 5)
     _need(w13_alpha, torch.float32, "w13_alpha", 1)
     _need(w2_alpha, torch.float32, "w2_alpha", 1)
     T, H = x.shape
     topk = topk_ids.shape[1]
     E = w13.shape[0]
-    I = w13.shape[1] // 2
-    if H % 16 or I % 16 or I == 0:
+    I = w13.shape[1] * 8
+    if H % 16 or H == 0 or I == 0:
         raise ValueError("moe_forward: H and I must be positive multiples of 16")
-    ldq_h, ldsf_h = operand_pitches(H)
-    ldq_i, ldsf_i = operand_pitches(I)
-    if (w13.shape != (E, 2 * I, ldq_h) or w13_sf.shape != (E, 2 * I, ldsf_h)
-            or w2.shape != (E, H, ldq_i) or w2_sf.shape != (E, H, ldsf_i)
+    s13, s13f = packed_shapes(E, H, 2 * I)
+    s2, s2f = packed_shapes(E, I, H)
+    if (tuple(w13.shape) != s13 or tuple(w13_sf.shape) != s13f
+            or tuple(w2.shape) != s2 or tuple(w2_sf.shape) != s2f
             or w13_alpha.shape != (E,) or w2_alpha.shape != (E,)
             or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
         raise ValueError("moe_forward: inconsistent shapes")

@@ -175,14 +175,14 @@ int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf) {
 int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int64_t K, int64_t N,
                           uint8_t* w_t, uint8_t* w_sf_t, hipStream_t stream) {
     if (E < 0 || K <= 0 || N <= 0) return NVFP4_EINVAL;
-    if (K % 16 || E > 65535) return NVFP4_ESHAPE;
+    if (K % 16 || N % 16 || E > 65535) return NVFP4_ESHAPE;
     if (E == 0) return NVFP4_OK;
     if (!w || !w_sf || !w_t || !w_sf_t) return NVFP4_EINVAL;
     if (!aligned(w_t, 16) || !aligned(w_sf_t, 8)) return NVFP4_EINVAL;
     int dv = check_device();
     if (dv) return dv;
-    NVFP4_TRY(launch_transpose_bytes(w, E, K / 2, N, w_t, pitch_q(K), stream));
-    NVFP4_TRY(launch_transpose_bytes(w_sf, E, K / 16, N, w_sf_t, pitch_sf(K), stream));
+    NVFP4_TRY(launch_pack_weights(w, E, K / 2, N, w_t, pitch_q(K), 64, stream));
+    NVFP4_TRY(launch_pack_weights(w_sf, E, K / 16, N, w_sf_t, pitch_sf(K), 8, stream));
     return NVFP4_OK;
 }
 

@@ -14,9 +14,10 @@
 // Operands. A rows and B rows (one per weight column: the weights in the
 // byte-transposed layout, as the pages' GEMM consumed B column-major) are
 // both K-packed, 64 bytes per 128-element K step, with their E4M3 scales
-// alongside. Tiles move from HBM to LDS by buffer loads that write LDS
-// directly (no staging registers; out-of-range offsets read zeros), four
-// stages deep (36 KB each).
+// alongside; B comes in 16-row blocks whose K steps are contiguous (1 KB per
+// step), so every load instruction of B reads one contiguous kilobyte. Tiles
+// move from HBM to LDS by buffer loads that write LDS directly (no staging
+// registers; out-of-range offsets read zeros), four stages deep (36 KB each).
 //
 // LDS layout. A stage holds 256 A rows and 256 B rows of 64 bytes, unpadded;
 // the four 16-byte chunks of a row are XOR-swizzled with bits 2-3 of the row,
@@ -136,7 +137,7 @@ void gemm_kernel(GemmParams p) {
         const int row = (4 * wave + t) * 16 + (lane >> 2);
         const int chunk = swz(row, lane & 3);
         a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
-        b_off[t] = (uint32_t)(b_src(row) * ldq + 16 * chunk);
+        b_off[t] = (uint32_t)(wq_row(b_src(row), ldq) + 16 * chunk);
     }
     // scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 + lane:
     // row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the step's 8
@@ -145,27 +146,29 @@ void gemm_kernel(GemmParams p) {
     for (int t = 0; t < 2; ++t) {
         const int row = (2 * wave + t) * 32 + (lane >> 1);
         asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
-        bsf_off[t] = (uint32_t)(b_src(row) * ldsf + 4 * (lane & 1));
+        bsf_off[t] = (uint32_t)(wsf_row(b_src(row), ldsf) + 4 * (lane & 1));
     }
 
     const int nk = (int)(ldq / KB);
     auto issue_stage = [&](int ks) {
         uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-        const uint32_t kd = (uint32_t)ks * KB, ksf = (uint32_t)ks * 8;
+        // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
+        const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
+        const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)ks * kWsfStep;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
-                                                     16, a_off[t], kd, 0, 0);
+                                                     16, a_off[t], kda, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
-                                                     16, b_off[t], kd, 0, 0);
+                                                     16, b_off[t], kdb, 0, 0);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + t) * 256), 4, asf_off[t], ksf, 0, 0);
+                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + t) * 256), 4, asf_off[t], ksa, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (2 * wave + t) * 256), 4,
-                bsf_off[t], ksf, 0, 0);
+                bsf_off[t], ksb, 0, 0);
         }
     };
 

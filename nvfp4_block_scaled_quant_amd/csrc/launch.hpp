@@ -44,10 +44,22 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int3
 __host__ __device__ inline int64_t pitch_q(int64_t K) { return (K / 2 + 63) / 64 * 64; }
 __host__ __device__ inline int64_t pitch_sf(int64_t K) { return (K / 16 + 7) / 8 * 8; }
 
-// Byte transpose of E matrices (R, C) -> (C, ldo) with zero padding of the
-// rows from R to ldo bytes.
-hipError_t launch_transpose_bytes(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
-                                  int64_t ldo, hipStream_t s);
+// Packed weight layout. A weight matrix is N rows (one per output column) of
+// pitch_q(K) bytes, K-packed; rows are grouped in blocks of 16, and inside a
+// block the 64 bytes of one 128-element K step of all 16 rows are stored
+// together (1 KB), step after step. Scales likewise: 8 bytes per row and step,
+// 128 bytes per block and step. So one K step of a 16-row block, the unit an
+// MFMA operand load covers, is contiguous.
+constexpr int kWqStep = 16 * 64;      // bytes of one K step of a 16-row block
+constexpr int kWsfStep = 16 * 8;
+__host__ __device__ inline int64_t wq_row(int64_t n, int64_t ldq) { return (n >> 4) * 16 * ldq + (n & 15) * 64; }
+__host__ __device__ inline int64_t wsf_row(int64_t n, int64_t ldsf) { return (n >> 4) * 16 * ldsf + (n & 15) * 8; }
+
+// Canonical (R, C) byte matrices (E of them, R = K-packed rows, C = N) into
+// the packed layout: element (r, c) goes to row c, byte r of a row of pitch
+// ldo, in steps of sw bytes (64 for data, 8 for scales); padding bytes are 0.
+hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
+                               int64_t ldo, int sw, hipStream_t s);
 
 // Column-block quantization of E weight matrices (E, K, N) with per-matrix amax.
 hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,

@@ -84,10 +84,11 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     }
 }
 
-// Byte transpose of E matrices (R, C) -> (C, ldo), rows zero-padded from R to
-// ldo bytes, through a 64 x 64 LDS tile.
-__global__ __launch_bounds__(kThreads) void transpose_bytes_kernel(
-    const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out, int64_t ldo) {
+// Canonical (R, C) byte matrices -> the packed weight layout (launch.hpp),
+// through a 64 x 64 LDS tile: reads along C and writes along R are coalesced.
+__global__ __launch_bounds__(kThreads) void pack_weights_kernel(
+    const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out, int64_t ldo,
+    int sw) {
     __shared__ uint8_t tile[64][65];
     const int64_t e = blockIdx.z;
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(kThreads) void transpose_bytes_kernel(
     for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
         const int cc = i >> 6, rr = i & 63;
         const int64_t r = r0 + rr, c = c0 + cc;
-        if (c < C && r < ldo) dst[c * ldo + r] = tile[rr][cc];
+        if (c < C && r < ldo)
+            dst[(c >> 4) * 16 * ldo + (r / sw) * 16 * sw + (c & 15) * sw + r % sw] = tile[rr][cc];
     }
 }
 
@@ -177,12 +179,13 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int3
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_bytes(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
-                                  int64_t ldo, hipStream_t s) {
+hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
+                               int64_t ldo, int sw, hipStream_t s) {
     if (E <= 0 || C <= 0) return hipSuccess;
     // rows of the output beyond R (padding) are covered by extra row tiles
     const int64_t rt = (ldo + 63) / 64, ct = (C + 63) / 64;
-    transpose_bytes_kernel<<<dim3((unsigned)ct, (unsigned)rt, (unsigned)E), kThreads, 0, s>>>(in, R, C, out, ldo);
+    pack_weights_kernel<<<dim3((unsigned)ct, (unsigned)rt, (unsigned)E), kThreads, 0, s>>>(in, R, C, out, ldo,
+                                                                                        sw);
     return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@
 //   (c, q) = (lane % 16, lane / 16) loads 16 contiguous bytes (32 K values,
 //   [32q, 32q + 32) of the step) from each of 8 weight rows: column c of the
 //   8 MFMA column blocks f (block f holds weight rows 16f + c of the slab).
+//   In the packed weight layout one such load instruction (16 rows x 64 bytes
+//   of one K step of a 16-row block) reads one contiguous kilobyte.
 //   Dword s of a load is the B operand of v_mfma_f32_16x16x32_f16 for
 //   substep s (K values 32q + 8s .. +8 of the step); A rows are read from LDS
 //   with the same K permutation, so every k meets its own partner. Nothing of
@@ -104,8 +106,8 @@ void skinny_kernel(GemmParams p) {
             ok[f] = row < N;
             row = ok[f] ? row : 0;
         }
-        boff[f] = (uint32_t)(row * ldq + 16 * q);
-        sfoff[f] = (uint32_t)(row * ldsf + 2 * q);
+        boff[f] = (uint32_t)(wq_row(row, ldq) + 16 * q);
+        sfoff[f] = (uint32_t)(wsf_row(row, ldsf) + 2 * q);
     }
 
     const int nsteps = (int)(ldq / 64);
@@ -122,7 +124,7 @@ void skinny_kernel(GemmParams p) {
         uint32_t s[NB];
     };
     auto load = [&](int st, Raw& rw) {
-        const uint32_t kd = (uint32_t)st * 64, ksf = (uint32_t)st * 8;
+        const uint32_t kd = (uint32_t)st * kWqStep, ksf = (uint32_t)st * kWsfStep;
 #pragma unroll
         for (int f = 0; f < NB; ++f) {
             rw.w[f] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[f], kd, 0);

@@ -114,16 +114,26 @@ def test_quantize_weights_full_expert(nv):
         assert (q[0] == rq).all()
 
 
-@pytest.mark.parametrize("E,K,N", [(1, 16, 16), (3, 272, 40), (2, 256, 200), (1, 7168, 96),
-                                   (4, 400, 130)])
-def test_prepack_weights_is_a_padded_transpose(nv, E, K, N):
-    # pure data movement: byte-exact against a NumPy transpose, padding zero
+def _packed_layout(a, pitch, sw):
+    # canonical (E, R, C) -> rows of C, padded to `pitch` bytes, in 16-row
+    # blocks whose `sw`-byte K steps are stored together
+    E, R, C = a.shape
+    rows = np.zeros((E, C, pitch), np.uint8)
+    rows[:, :, :R] = a.transpose(0, 2, 1)
+    return rows.reshape(E, C // 16, 16, pitch // sw, sw).transpose(0, 1, 3, 2, 4)
+
+
+@pytest.mark.parametrize("E,K,N", [(1, 16, 16), (3, 272, 48), (2, 256, 208), (1, 7168, 96),
+                                   (4, 400, 128)])
+def test_prepack_weights_layout(nv, E, K, N):
+    # pure data movement: byte-exact against NumPy's transpose and reshape,
+    # padding bytes zero
     rng = np.random.default_rng(E + K + N)
     q = rng.integers(0, 256, (E, K // 2, N)).astype(np.uint8)
     sf = rng.integers(0, 256, (E, K // 16, N)).astype(np.uint8)
     q_t, sf_t = (to_host(t) for t in nv.prepack_weights(to_dev(q), to_dev(sf)))
     ldq, ldsf = nv.operand_pitches(K)
-    assert q_t.shape == (E, N, ldq) and sf_t.shape == (E, N, ldsf)
-    assert (q_t[:, :, :K // 2] == q.transpose(0, 2, 1)).all()
-    assert (sf_t[:, :, :K // 16] == sf.transpose(0, 2, 1)).all()
-    assert (q_t[:, :, K // 2:] == 0).all() and (sf_t[:, :, K // 16:] == 0).all()
+    assert q_t.shape == (E, N // 16, ldq // 64, 16, 64)
+    assert sf_t.shape == (E, N // 16, ldsf // 8, 16, 8)
+    assert (q_t == _packed_layout(q, ldq, 64)).all()
+    assert (sf_t == _packed_layout(sf, ldsf, 8)).all()

@@ -110,6 +110,7 @@ def test_operand_pitches(nv):
 def test_prepack_argument_errors(nv):
     f = lib(nv).nvfp4_prepack_weights
     assert f(p(A16), p(A16), 2, 24, 16, p(A16), p(A16), None) == 2        # K % 16
+    assert f(p(A16), p(A16), 2, 32, 24, p(A16), p(A16), None) == 2        # N % 16
     assert f(p(A16), p(A16), -1, 32, 16, p(A16), p(A16), None) == 1
     assert f(p(A16), p(A16), 2, 32, 0, p(A16), p(A16), None) == 1
     assert f(p(0), p(A16), 2, 32, 16, p(A16), p(A16), None) == 1
