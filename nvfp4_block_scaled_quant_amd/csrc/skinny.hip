@@ -10,10 +10,11 @@
 //   columns). Its 16 A rows are staged once in LDS, still packed, while the
 //   first weight loads are already in flight.
 // * Each wave streams its own 128 weight rows over the whole of K, two K
-//   steps in flight, and finishes its outputs by itself (no cross-wave
-//   reduction). Per 128-element K step, lane (c, q) = (lane % 16, lane / 16)
-//   loads 16 contiguous bytes (32 K values, [32q, 32q + 32) of the step) from
-//   each of 8 weight rows: column c of the 8 MFMA column blocks f (block f
+//   steps in flight, with non-temporal loads (the weights are read once),
+//   and finishes its outputs by itself (no cross-wave reduction). Per
+//   128-element K step, lane (c, q) = (lane % 16, lane / 16) loads 16
+//   contiguous bytes (32 K values, [32q, 32q + 32) of the step) from each of
+//   8 weight rows: column c of the 8 MFMA column blocks f (block f
 //   holds weight rows 16f + c of the wave's 128). In the packed weight layout
 //   one such load instruction (16 rows x 64 bytes of one K step of a 16-row
 //   block) reads one contiguous kilobyte.
@@ -41,6 +42,8 @@ constexpr int NB = 8;             // MFMA column blocks per lane (weight rows 16
 constexpr int WROWS = 16 * NB;    // weight rows per wave
 constexpr int GB = NB / 2;        // L1: gate blocks (and as many up blocks) per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr int kStreamNT = 2;      // buffer-load cache policy: non-temporal (read once)
+constexpr int kStagger = 13;      // start-step offset between consecutive waves
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
@@ -98,19 +101,26 @@ void skinny_kernel(GemmParams p) {
     // a wave whose columns all lie beyond the matrix streams nothing
     const bool active = (MODE == kGemmL1) ? (col0 < p.I) : (col0 < N);
     const int nsteps = active ? (int)(ldq / 64) : 0;
+    // Waves start at different K steps and wrap around, so that at any moment
+    // the concurrent streams spread over the memory channels instead of all
+    // starting at the same offset of their blocks. The order of the fp32
+    // partial sums is fixed per output column.
+    const int s0 = nsteps ? (int)(((int64_t)blockIdx.x * NW + wave) * kStagger % nsteps) : 0;
+    auto kstep = [&](int i) { return i + s0 < nsteps ? i + s0 : i + s0 - nsteps; };
 
     struct Raw {
         u32x4 w[NB];
         uint32_t s[NB];
     };
-    auto load = [&](int st, Raw& rw) {
+    auto load = [&](int i, Raw& rw) {
         // the step offsets go to the scalar offset operand: keep them uniform
+        const int st = kstep(i);
         const uint32_t kd = __builtin_amdgcn_readfirstlane((uint32_t)st * kWqStep);
         const uint32_t ksf = __builtin_amdgcn_readfirstlane((uint32_t)st * kWsfStep);
 #pragma unroll
         for (int f = 0; f < NB; ++f) {
-            rw.w[f] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[f], kd, 0);
-            rw.s[f] = __builtin_amdgcn_raw_buffer_load_b16(rbsf, sfoff[f], ksf, 0);
+            rw.w[f] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[f], kd, kStreamNT);
+            rw.s[f] = __builtin_amdgcn_raw_buffer_load_b16(rbsf, sfoff[f], ksf, kStreamNT);
         }
     };
 
@@ -180,7 +190,8 @@ void skinny_kernel(GemmParams p) {
 #pragma unroll
     for (int f = 0; f < NB; ++f) acc[f] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int st, const Raw& rw) {
+    auto compute = [&](int i, const Raw& rw) {
+        const int st = kstep(i);
         // A row c, bytes [16q, 16q + 16) of the step; scale groups 2q, 2q + 1
         const u32x4 aw = *reinterpret_cast<const u32x4*>(sA + c * a_pitch + st * 64 + 16 * q);
         uint32_t as = (uint32_t)sAsf[c * ldsf + st * 8 + 2 * q] |
@@ -201,7 +212,7 @@ void skinny_kernel(GemmParams p) {
         }
     };
 
-    // two steps in flight: r0 holds step st, r1 step st + 1
+    // two steps in flight: r0 holds loop step st, r1 step st + 1
     while (st < nsteps) {
         compute(st, r0);
         ++st;
