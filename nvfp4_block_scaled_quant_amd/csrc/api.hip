@@ -283,12 +283,19 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
 
     // 1. routing tables + tile list (also zeroes both amax slots)
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_ROUTE));
+    // A small x is quantized by a second work-group of the routing launch
+    // (stage 2 is then empty); a larger one by the amax and block kernels.
+    const bool small_x = T * H <= kSmallQuantMax;
+    const SmallQuant sq = {x, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
     NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
-                           slot_row, tiles, num_tiles, amax, 2, stream));
+                           slot_row, tiles, num_tiles, amax, 2, small_x ? &sq : nullptr, stream));
     // 2. quantize x
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
-    NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
-    NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, pitch_q(H), xsf, pitch_sf(H), gs1, stream));
+    if (!small_x) {
+        NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
+        NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, pitch_q(H), xsf, pitch_sf(H), gs1,
+                                    stream));
+    }
     // 3. L1 grouped GEMM with fused SiLU(gate) * up
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
     GemmParams p1 = {};

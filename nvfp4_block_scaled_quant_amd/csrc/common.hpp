@@ -233,4 +233,24 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&
     c[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
+// Quantize block b of a row-major (rows, K) bf16 matrix (groups = K / 16
+// blocks per row) into rows of pitch ldq (packed) and ldsf (scales).
+__device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ x, int64_t b,
+                                                   int64_t groups, const QuantScales& qs,
+                                                   uint8_t* __restrict__ q, int64_t ldq,
+                                                   uint8_t* __restrict__ sf, int64_t ldsf) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
+    const u32x4 v0 = src[0];
+    const u32x4 v1 = src[1];
+    const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    uint32_t packed[2];
+    const uint32_t code = quantize_block16(w, qs, packed);
+    u32x2 out;
+    out[0] = packed[0];
+    out[1] = packed[1];
+    const int64_t r = b / groups, g = b - r * groups;
+    *reinterpret_cast<u32x2*>(q + r * ldq + g * 8) = out;
+    sf[r * ldsf + g] = (uint8_t)code;
+}
+
 }  // namespace nvfp4

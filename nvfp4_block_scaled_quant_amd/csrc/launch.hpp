@@ -68,10 +68,23 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
 
 // Routing tables and the tile list (single work-group kernel). Also zeroes
 // `zero_slots` (n_zero words) before anything else in the layer runs.
-hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM,
-                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
-                        int32_t* slot_row, Tile* tiles, int32_t* num_tiles,
-                        uint32_t* zero_slots, int n_zero, hipStream_t s);
+// Quantization of a small activation done inside the routing launch, by a
+// second work-group (amax and the block pass in one work-group).
+struct SmallQuant {
+    const uint16_t* x;
+    int64_t M, K;
+    uint8_t* q;
+    int64_t ldq;
+    uint8_t* sf;
+    int64_t ldsf;
+    float* gs;
+};
+constexpr int64_t kSmallQuantMax = 1 << 17;   // elements: larger inputs take the two-kernel path
+
+hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
+                        int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
+                        hipStream_t s);
 
 // y[t] = bf16(sum_j w[t][j] * o2[slot_row[t*topk+j]]) for rows that exist.
 hipError_t launch_combine(const float* o2, const int32_t* slot_row, const float* weights,

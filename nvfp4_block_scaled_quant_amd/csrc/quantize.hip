@@ -68,20 +68,8 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const int64_t groups = K / 16;
     const int64_t nblocks = rows * groups;
     for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
-         b += (int64_t)gridDim.x * kThreads) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
-        const u32x4 v0 = src[0];
-        const u32x4 v1 = src[1];
-        const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        uint32_t packed[2];
-        const uint32_t code = quantize_block16(w, qs, packed);
-        u32x2 out;
-        out[0] = packed[0];
-        out[1] = packed[1];
-        const int64_t r = b / groups, g = b - r * groups;
-        *reinterpret_cast<u32x2*>(q + r * ldq + g * 8) = out;
-        sf[r * ldsf + g] = (uint8_t)code;
-    }
+         b += (int64_t)gridDim.x * kThreads)
+        quantize_row_block(x, b, groups, qs, q, ldq, sf, ldsf);
 }
 
 // Canonical (R, C) byte matrices -> the packed weight layout (launch.hpp),

@@ -12,7 +12,10 @@
 //
 // Routing runs in a single 1024-thread work-group: it is a few microseconds of
 // integer work on at most a few tens of thousands of slots and it produces the
-// whole tile list on the device, so the host never waits for counts.
+// whole tile list on the device, so the host never waits for counts. For a
+// small batch further work-groups of the same launch quantize the layer input
+// (each takes the amax of the whole input, then does its share of the block
+// pass), saving two launches.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,7 +30,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int32_t* __restrict__ ids, int64_t S, int E, int BM, int nbits,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ slot_row, Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles,
-    uint32_t* __restrict__ zero_slots, int n_zero) {
+    uint32_t* __restrict__ zero_slots, int n_zero, SmallQuant xq) {
+    if (blockIdx.x > 0) {
+        // small activation: every quantization work-group reduces the amax of
+        // all of x (a few hundred KB at most, from L2) and then quantizes its
+        // own share of the 16-element blocks
+        __shared__ uint32_t wmax[kWaves];
+        const int tid = threadIdx.x;
+        const int64_t n = xq.M * xq.K;
+        const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
+        uint32_t m = 0;
+        for (int64_t i = tid; i < n / 8; i += kRouteThreads) {
+            const u32x4 w = v[i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7FFFu, (w[c] >> 16) & 0x7FFFu));
+        }
+        m = wave_max_u32(m);
+        if ((tid & 63) == 0) wmax[tid >> 6] = m;
+        __syncthreads();
+        m = wmax[0];
+        for (int w = 1; w < kWaves; ++w) m = max(m, wmax[w]);
+        const QuantScales qs = make_scales(__uint_as_float(m << 16));
+        if (blockIdx.x == 1 && tid == 0) *xq.gs = qs.gs;
+        const int64_t groups = xq.K / 16;
+        for (int64_t b = (int64_t)(blockIdx.x - 1) * kRouteThreads + tid; b < xq.M * groups;
+             b += (int64_t)(gridDim.x - 1) * kRouteThreads)
+            quantize_row_block(xq.x, b, groups, qs, xq.q, xq.ldq, xq.sf, xq.ldsf);
+        return;
+    }
     extern __shared__ int32_t lds[];
     int32_t* cnt = lds;
     int32_t* off = cnt + E;
@@ -48,18 +78,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
 
-    // exclusive scans of counts and of tiles per expert
-    if (tid == 0) {
+    // exclusive scans of counts and of tiles per expert: wave 0, 64 experts at
+    // a time, shuffle-based inclusive scan within the wave
+    if (wave == 0) {
         int acc = 0, tacc = 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = acc;
-            tile_base[e] = tacc;
-            acc += cnt[e];
-            tacc += (cnt[e] + BM - 1) / BM;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const int c = (e < E) ? cnt[e] : 0;
+            int ic = c, it = (c + BM - 1) / BM;
+            const int t = it;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int uc = __shfl_up(ic, d), ut = __shfl_up(it, d);
+                if (lane >= d) { ic += uc; it += ut; }
+            }
+            if (e < E) {
+                off[e] = acc + ic - c;
+                tile_base[e] = tacc + it - t;
+            }
+            acc += __shfl(ic, 63);
+            tacc += __shfl(it, 63);
         }
-        off[E] = acc;
-        tile_base[E] = tacc;
-        *num_tiles = tacc;
+        if (lane == 0) {
+            off[E] = acc;
+            tile_base[E] = tacc;
+            *num_tiles = tacc;
+        }
     }
     __syncthreads();
     for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
@@ -150,13 +194,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
-                        int32_t* num_tiles, uint32_t* zero_slots, int n_zero, hipStream_t s) {
+                        int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
+                        hipStream_t s) {
     (void)topk;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
     const size_t lds = sizeof(int32_t) * ((size_t)E * (3 + kWaves) + 1);
-    route_kernel<<<1, kRouteThreads, lds, s>>>(ids, S, E, BM, nbits, counts, offsets, sorted_slot,
-                                               slot_row, tiles, num_tiles, zero_slots, n_zero);
+    const SmallQuant none = {};
+    // work-groups 1.. quantize the small activation, one 16-element block per thread
+    const int64_t qgroups = xq ? (xq->M * (xq->K / 16) + kRouteThreads - 1) / kRouteThreads : 0;
+    route_kernel<<<(unsigned)(1 + qgroups), kRouteThreads, lds, s>>>(ids, S, E, BM, nbits, counts, offsets, sorted_slot,
+                                                        slot_row, tiles, num_tiles, zero_slots, n_zero,
+                                                        xq ? *xq : none);
     return hipGetLastError();
 }
 
