@@ -66,10 +66,8 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
                              const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
                              hipStream_t s);
 
-// Routing tables and the tile list (single work-group kernel). Also zeroes
-// `zero_slots` (n_zero words) before anything else in the layer runs.
-// Quantization of a small activation done inside the routing launch, by a
-// second work-group (amax and the block pass in one work-group).
+// Quantization of a small activation done inside the routing launch by extra
+// work-groups (each reduces the whole amax, then quantizes its share).
 struct SmallQuant {
     const uint16_t* x;
     int64_t M, K;
@@ -81,6 +79,9 @@ struct SmallQuant {
 };
 constexpr int64_t kSmallQuantMax = 1 << 17;   // elements: larger inputs take the two-kernel path
 
+// Routing tables and the tile list (one work-group), plus the quantization of
+// *xq when xq is not null. Also zeroes `zero_slots` (n_zero words) before
+// anything else in the layer runs.
 hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
                         int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
