@@ -251,6 +251,12 @@ __device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ 
     const int64_t r = b / groups, g = b - r * groups;
     *reinterpret_cast<u32x2*>(q + r * ldq + g * 8) = out;
     sf[r * ldsf + g] = (uint8_t)code;
+    if (g == groups - 1) {
+        // the row's padding up to the pitches is written as zeros, so that a
+        // GEMM reading whole 128-element steps sees zero scales and data there
+        for (int64_t j = groups * 8; j < ldq; j += 8) *reinterpret_cast<u32x2*>(q + r * ldq + j) = (u32x2){0u, 0u};
+        for (int64_t j = groups; j < ldsf; ++j) sf[r * ldsf + j] = 0;
+    }
 }
 
 }  // namespace nvfp4

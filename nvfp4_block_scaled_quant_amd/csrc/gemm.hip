@@ -36,8 +36,11 @@
 // sorted row, row count); the grid is sized for the worst case and idle
 // work-groups leave at once, so the host never waits for routing counts.
 // Invalid rows and columns of a tile read a valid row instead (their results
-// are never stored); in a partial last K step the scales of the missing
-// groups are zeroed, which zeroes whatever nibbles were read there.
+// are never stored). Rows are read in whole 128-element steps: the padding of
+// a partial last step is zero in both operands (the quantizers and the weight
+// prepack write it as zeros), so it adds nothing.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -88,7 +91,6 @@ void gemm_kernel(GemmParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int64_t K = p.K, N = p.N;
-    const int64_t Kg = K / 16;                               // real scale groups per row
     const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);      // padded row pitches
     const int ntn = (MODE == kGemmL1) ? (int)((p.I + 127) / 128) : (int)((N + BN - 1) / BN);
     const int tile_idx = blockIdx.x / ntn;
@@ -206,49 +208,51 @@ void gemm_kernel(GemmParams p) {
             fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
             sb[j] = *reinterpret_cast<const uint32_t*>(sBsf + vc * 8 + 4 * h);
         }
-        // partial last step: scale groups beyond K read zero scales
-        const int64_t g0 = (int64_t)ks * 8 + 4 * h;
-        if (g0 + 4 > Kg) {
-            uint32_t mask = 0;
+    };
+    // operands of substep s in registers s & 1
+    half8_t ha[2][4], hb[2][4];
+    auto deq = [&](int s, half8_t (&xa)[4], half8_t (&xb)[4]) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (g0 + b < Kg) mask |= 0xFFu << (8 * b);
+        for (int i = 0; i < 4; ++i)
+            xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sa[i] &= mask;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sb[j] &= mask;
-        }
+        for (int j = 0; j < 4; ++j)
+            xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
     };
 
-    // Pipeline: stages ks+1..ks+3 are in flight while step ks computes; the
-    // barrier before the fragment reads of step ks+1 (in substep 7) makes the
-    // other waves' DMA of that stage visible and frees buffer (ks-1) % 4.
+    // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
+    // substep s issues its 16 MFMAs with the dequant of substep s + 1 between
+    // them. Substep 7 starts with the wait for this wave's DMA of stage ks+1
+    // and the barrier (the other waves' DMA of it is then visible, and buffer
+    // (ks-1) % 4, which the next step refills, has been read by everyone),
+    // reads the fragments of step ks+1, and dequantizes substep 0 of step ks+1
+    // between its later MFMAs, so that no dequant runs outside an MFMA shadow.
+    // Scheduling barriers keep each substep's instructions together.
     for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     read_frags(0);
+    deq(0, ha[0], hb[0]);
 
-    for (int ks = 0; ks < nk; ++ks) {
-        if (ks + NSTAGE - 1 < nk) issue_stage(ks + NSTAGE - 1);
-        half8_t ha[2][4], hb[2][4];
-        auto deq = [&](int s, half8_t (&xa)[4], half8_t (&xb)[4]) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
-        };
-        deq(0, ha[0], hb[0]);
+    // One K step. Phase 0: steady state (refill a stage, wait until 24 loads
+    // remain, fetch the next step); 1 and 2: the last two refills have been
+    // issued (wait until 12 / 0 remain); 3: the last step. Every condition is a
+    // compile-time constant, so a step is one basic block the scheduler can
+    // interleave freely.
+    auto step = [&](int ks, auto mode_c) {
+        constexpr int PH = decltype(mode_c)::value;
+        if (PH == 0) issue_stage(ks + NSTAGE - 1);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            if (s < 7) deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
-            if (s == 7 && ks + 1 < nk) {
+            if (s < 7) {
+                deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
+            } else if (PH < 3) {
                 // this wave's DMA of stage ks+1 is done when at most the stages
-                // issued after it (up to two, 12 loads each) are outstanding
-                if (ks + NSTAGE - 1 < nk) __builtin_amdgcn_s_waitcnt(0x4F78);        // vmcnt(24)
-                else if (ks + NSTAGE - 2 < nk) __builtin_amdgcn_s_waitcnt(0x0F7C);   // vmcnt(12)
-                else __builtin_amdgcn_s_waitcnt(0x0F70);                             // vmcnt(0)
+                // issued after it are outstanding; lgkmcnt(0): its own fragment
+                // reads of this step are complete before it passes the barrier
+                if (PH == 0) __builtin_amdgcn_s_waitcnt(0x4078);        // vmcnt(24) lgkmcnt(0)
+                if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007C);        // vmcnt(12) lgkmcnt(0)
+                if (PH == 2) __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
                 lds_barrier();
                 read_frags(ks + 1);
             }
@@ -262,11 +266,27 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);       // four VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);       // five VALU
+                }
+            } else if (PH < 3) {
+                deq(0, ha[0], hb[0]);
+                // the fragment reads land under the first MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);          // the LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+#pragma unroll
+                for (int k = 0; k < 10; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    int ks = 0;
+    for (; ks + NSTAGE - 1 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
+    if (nk - ks == 3) step(ks++, std::integral_constant<int, 1>{});
+    if (nk - ks == 2) step(ks++, std::integral_constant<int, 2>{});
+    step(ks, std::integral_constant<int, 3>{});
     __syncthreads();
 
     // ---- epilogue ------------------------------------------------------------
