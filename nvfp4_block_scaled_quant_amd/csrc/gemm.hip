@@ -152,26 +152,30 @@ void gemm_kernel(GemmParams p) {
     }
 
     const int nk = (int)(ldq / KB);
-    auto issue_stage = [&](int ks) {
+    // part t (0..5) of the DMA of stage ks: t < 4 one A and one B data load,
+    // t = 4, 5 one A and one B scale load
+    auto issue_part = [&](int ks, int t) {
         uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
         // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
         const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
         const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)ks * kWsfStep;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        if (t < 4) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
                                                      16, a_off[t], kda, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
                                                      16, b_off[t], kdb, 0, 0);
+        } else {
+            const int u = t - 4;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + u) * 256), 4, asf_off[u], ksa, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (2 * wave + u) * 256), 4,
+                bsf_off[u], ksb, 0, 0);
         }
+    };
+    auto issue_stage = [&](int ks) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + t) * 256), 4, asf_off[t], ksa, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (2 * wave + t) * 256), 4,
-                bsf_off[t], ksb, 0, 0);
-        }
+        for (int t = 0; t < 6; ++t) issue_part(ks, t);
     };
 
     // ---- main loop ---------------------------------------------------------
@@ -241,9 +245,11 @@ void gemm_kernel(GemmParams p) {
     // interleave freely.
     auto step = [&](int ks, auto mode_c) {
         constexpr int PH = decltype(mode_c)::value;
-        if (PH == 0) issue_stage(ks + NSTAGE - 1);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
+            // the refill of stage ks+3 is spread over substeps 0..5: a burst of
+            // twelve LDS-DMA issues at once stalls the MFMA stream
+            if (PH == 0 && s < 6) issue_part(ks + NSTAGE - 1, s);
             if (s < 7) {
                 deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
             } else if (PH < 3) {
