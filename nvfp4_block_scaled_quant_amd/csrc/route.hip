@@ -171,16 +171,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < topk; ++j) {
-        const int32_t row = slot_row[t * topk + j];
-        if (row < 0) continue;
-        const float w = weights[t * topk + j];
-        const float4_t* src = reinterpret_cast<const float4_t*>(o2 + (int64_t)row * H + c0);
-        const float4_t a = src[0], b = src[1];
+    // slots in batches of 8: all their loads are issued before the sums, which
+    // still run in slot order
+    for (int j0 = 0; j0 < topk; j0 += 8) {
+        int32_t row[8];
+        float w[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] = acc[i] + w * a[i];
-            acc[4 + i] = acc[4 + i] + w * b[i];
+        for (int u = 0; u < 8; ++u) {
+            const bool in = j0 + u < topk;
+            row[u] = in ? slot_row[t * topk + j0 + u] : -1;
+            w[u] = in ? weights[t * topk + j0 + u] : 0.0f;
+        }
+        float4_t a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
+            b[u] = a[u];
+            if (row[u] >= 0) {
+                const float4_t* src = reinterpret_cast<const float4_t*>(o2 + (int64_t)row[u] * H + c0);
+                a[u] = src[0];
+                b[u] = src[1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (row[u] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i] = acc[i] + w[u] * a[u][i];
+                acc[4 + i] = acc[4 + i] + w[u] * b[u][i];
+            }
         }
     }
     u32x4 out;
