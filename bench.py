@@ -147,16 +147,25 @@ def decode_bytes(cfg, ids_np):
     return touched * per_expert + cfg.T * H * 2 * 2 + act, touched
 
 
-def cpu_baseline(cfg, experts=(0, 1)):
+def _oracle_expert_weights(args):
+    """Worker: one expert's weights quantized with the oracle's rule."""
+    import workloads as W
+    from oracle.quantize import quantize_weight_bf16
+    cfg, e = args
+    w13, w2 = W.expert_weights_bf16(cfg, e)
+    return e, quantize_weight_bf16(w13), quantize_weight_bf16(w2)
+
+
+def cpu_baseline(cfg, experts=tuple(range(24))):
     """The oracle's layer forward timed on a bounded sample of the prefill
     workload: all T tokens' x, but only the slots routed to `experts` (the other
     slots are skipped), with those experts' weights quantized by the oracle
-    (untimed). Reported as token-equivalents per second: sample slots / topk /
-    seconds."""
+    beforehand (untimed, in spawned worker processes). Reported as
+    token-equivalents per second: sample slots / topk / seconds."""
+    import multiprocessing as mp
     import numpy as np
     import workloads as W
     from oracle.moe import moe_forward
-    from oracle.quantize import quantize_weight_bf16
     x = W.activations(cfg)
     ids, wts = W.routing(cfg)
     keep = np.isin(ids, experts)
@@ -168,10 +177,12 @@ def cpu_baseline(cfg, experts=(0, 1)):
     w2sf = np.zeros((E, I // 16, H), np.uint8)
     w13a = np.zeros(E, np.float32)
     w2a = np.zeros(E, np.float32)
-    for e in experts:
-        w13, w2 = W.expert_weights_bf16(cfg, e)
-        w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16(w13)
-        w2q[e], w2sf[e], w2a[e] = quantize_weight_bf16(w2)
+    nproc = max(1, min(len(experts), 16, len(os.sched_getaffinity(0))))
+    with mp.get_context("spawn").Pool(nproc) as pool:
+        for e, (q1, s1, a1), (q2, s2, a2) in pool.imap_unordered(
+                _oracle_expert_weights, [(cfg, e) for e in experts]):
+            w13q[e], w13sf[e], w13a[e] = q1, s1, a1
+            w2q[e], w2sf[e], w2a[e] = q2, s2, a2
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -186,8 +197,8 @@ def cpu_baseline(cfg, experts=(0, 1)):
             "blas_threads": blas_threads, "kind": "oracle", "seconds": dt,
             "sample": (f"prefill workload (T={cfg.T}, H={H}, I={I}, E={E}, top-{cfg.topk}): all "
                        f"tokens' x quantized, only the {slots} slots routed to experts "
-                       f"{list(experts)} run through L1/SiLU/requant/L2/combine; value = "
-                       f"slots/topk per second (token-equivalents); float64 BLAS matmuls "
+                       f"{experts[0]}..{experts[-1]} run through L1/SiLU/requant/L2/combine; "
+                       f"value = slots/topk per second (token-equivalents); float64 BLAS matmuls "
                        f"multithreaded, the rest single-threaded NumPy")}
 
 
