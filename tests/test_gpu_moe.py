@@ -166,3 +166,64 @@ def test_repeat_is_bit_identical(nv):
     cfg = W.small_layer("rep", T=200, H=512, I=256, E=8, topk=4, seed=12)
     g = run_gpu_layer(nv, make_layer(cfg), repeat=3)
     assert all((y == g["ys"][0]).all() for y in g["ys"])
+
+
+# ---- degenerate and boundary cases -------------------------------------------
+
+def test_empty_batch(nv):
+    # T = 0: nothing to do, y is (0, H)
+    import torch
+    cfg = W.small_layer("empty", T=4, H=256, I=128, E=4, topk=2, seed=21)
+    L = make_layer(cfg)
+    from helpers import gpu_packed_weights
+    pw = gpu_packed_weights(nv, L)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    wts = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    y = nv.moe_forward(x, ids, wts, pw["w13"], pw["w13_sf"], pw["w13a"], pw["w2"], pw["w2_sf"], pw["w2a"])
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 256)
+
+
+def test_all_zero_input(nv):
+    # x == 0: gs1 = 0, every scale byte and nibble 0, act = 0, gs2 = 0, y = +0
+    cfg = W.small_layer("zero", T=40, H=256, I=128, E=4, topk=2, seed=22)
+    L = make_layer(cfg)
+    L["x"] = np.zeros_like(L["x"])
+    g = run_gpu_layer(nv, L)
+    r = run_oracle_layer(L)
+    assert g["gs1"] == 0 and g["gs2"] == 0
+    assert not g["xq"].any() and not g["xsf"].any()
+    assert (g["y"] == 0).all()
+    assert (r["y"] == 0).all()
+
+
+def test_one_token_every_expert(nv):
+    # top-k = E: the single token visits every expert once (weight streaming)
+    cfg = W.small_layer("allexp", T=1, H=512, I=256, E=8, topk=8, seed=23)
+    compare_layer(nv, make_layer(cfg), "one token, top-k = E")
+
+
+def test_single_expert(nv):
+    # E = 1, top-1: one expert, two 256-row tiles (256 + 44)
+    cfg = W.small_layer("oneexp", T=300, H=256, I=128, E=1, topk=1, seed=24)
+    compare_layer(nv, make_layer(cfg), "single expert")
+
+
+def test_tile_boundaries(nv):
+    # experts with exactly 256 and 257 slots: a full tile, and a full tile plus
+    # a one-row tile
+    cfg = W.small_layer("tiles", T=513, H=256, I=128, E=2, topk=1, seed=25)
+    L = make_layer(cfg)
+    ids = np.zeros((513, 1), np.int32)
+    ids[256:] = 1
+    L["ids"] = ids
+    g, _, _ = compare_layer(nv, L, "tile boundaries")
+    assert list(g["counts"]) == [256, 257]
+
+
+@pytest.mark.parametrize("T", [32, 33])
+def test_path_switch_boundary(nv, T):
+    # S = 16 * E takes the weight-streaming kernels, one more slot the tiled GEMM
+    cfg = W.small_layer(f"switch{T}", T=T, H=512, I=256, E=4, topk=2, seed=26 + T)
+    compare_layer(nv, make_layer(cfg), f"path switch T={T}")
