@@ -188,9 +188,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             a[u] = (float4_t){0.f, 0.f, 0.f, 0.f};
             b[u] = a[u];
             if (row[u] >= 0) {
+                // each L2 row is read once: non-temporal loads
                 const float4_t* src = reinterpret_cast<const float4_t*>(o2 + (int64_t)row[u] * H + c0);
-                a[u] = src[0];
-                b[u] = src[1];
+                a[u] = __builtin_nontemporal_load(src);
+                b[u] = __builtin_nontemporal_load(src + 1);
             }
         }
 #pragma unroll
