@@ -24,6 +24,7 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kWaves = kRouteThreads / 64;
+constexpr int kIdBatches = 16;     // batches of 64 ids a lane holds at once
 
 // Dynamic LDS: cnt[E], off[E+1], run[E], wcnt[kWaves][E]
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
@@ -61,20 +62,50 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     extern __shared__ int32_t lds[];
     int32_t* cnt = lds;
     int32_t* off = cnt + E;
-    int32_t* run = off + E + 1;
-    int32_t* wcnt = run + E;
+    int32_t* wcnt = off + E + 1;                     // [kWaves][E]: counts, then running positions
     __shared__ int32_t tile_base[kMaxExperts + 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    // wave w owns the contiguous slot range [s_lo, s_hi): the sorted order is
+    // stable because the waves' ranges are in slot order and each wave scatters
+    // its own range in order
+    const int64_t per = (S + kWaves - 1) / kWaves;
+    const int64_t s_lo = min(S, (int64_t)wave * per), s_hi = min(S, s_lo + per);
     for (int i = tid; i < n_zero; i += kRouteThreads) zero_slots[i] = 0u;
-    for (int e = tid; e < E; e += kRouteThreads) { cnt[e] = 0; run[e] = 0; }
+    for (int i = tid; i < kWaves * E; i += kRouteThreads) wcnt[i] = 0;
     __syncthreads();
 
-    // histogram
-    for (int64_t s = tid; s < S; s += kRouteThreads) {
-        const int e = ids[s];
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    // ids in super-chunks of kIdBatches batches of 64 slots, all loads of a
+    // super-chunk in flight together (a loop of dependent loads would pay the
+    // memory latency once per batch)
+    int ids_r[kIdBatches];
+    auto load_ids = [&](int64_t c0) {
+#pragma unroll
+        for (int u = 0; u < kIdBatches; ++u) {
+            const int64_t s = c0 + 64 * u + lane;
+            ids_r[u] = (s < s_hi) ? ids[s] : -1;
+        }
+    };
+    // per-wave histograms
+    for (int64_t c0 = s_lo; c0 < s_hi; c0 += 64 * kIdBatches) {
+        load_ids(c0);
+#pragma unroll
+        for (int u = 0; u < kIdBatches; ++u) {
+            const int e = ids_r[u];
+            if (e >= 0 && e < E) atomicAdd(&wcnt[wave * E + e], 1);
+        }
+    }
+    __syncthreads();
+    // totals, and each wave's exclusive base within an expert
+    for (int e = tid; e < E; e += kRouteThreads) {
+        int acc = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = wcnt[w * E + e];
+            wcnt[w * E + e] = acc;
+            acc += c;
+        }
+        cnt[e] = acc;
     }
     __syncthreads();
 
@@ -120,14 +151,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         }
     }
 
-    // stable scatter: chunks of kRouteThreads slots in order; inside a chunk a
-    // slot's rank is (same-expert slots of earlier waves) + (same-expert lanes
-    // below it in its own wave, found by matching the id bit by bit)
-    for (int64_t c0 = 0; c0 < S; c0 += kRouteThreads) {
-        for (int i = tid; i < kWaves * E; i += kRouteThreads) wcnt[i] = 0;
-        __syncthreads();
-        const int64_t s = c0 + tid;
-        const int e = (s < S) ? ids[s] : -1;
+    // stable scatter, wave by wave with no further barrier: 64 slots at a time,
+    // a slot's position is its expert's start + this wave's base + the slots of
+    // the same expert before it (earlier batches: the running count in LDS;
+    // this batch: lanes below it with the same id, matched bit by bit)
+    int32_t* run = wcnt + wave * E;
+    for (int64_t c00 = s_lo; c00 < s_hi; c00 += 64 * kIdBatches) {
+      load_ids(c00);
+#pragma unroll
+      for (int u = 0; u < kIdBatches; ++u) {
+        const int64_t c0 = c00 + 64 * u;
+        if (c0 >= s_hi) break;
+        const int64_t s = c0 + lane;
+        const int e = ids_r[u];
         const bool valid = (e >= 0 && e < E);
         uint64_t match = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
@@ -138,24 +174,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         const int rank = __popcll(match & below);
         const int total = __popcll(match);
-        if (valid && rank == total - 1) wcnt[wave * E + e] = total;
-        __syncthreads();
         if (valid) {
-            int base = run[e];
-            for (int w = 0; w < wave; ++w) base += wcnt[w * E + e];
-            const int pos = off[e] + base + rank;
+            const int pos = off[e] + run[e] + rank;
             sorted_slot[pos] = (int32_t)s;
             slot_row[s] = pos;
-        } else if (s < S) {
+        } else if (s < s_hi) {
             slot_row[s] = -1;
         }
-        __syncthreads();
-        for (int ee = tid; ee < E; ee += kRouteThreads) {
-            int add = 0;
-            for (int w = 0; w < kWaves; ++w) add += wcnt[w * E + ee];
-            run[ee] += add;
-        }
-        __syncthreads();
+        // every lane has read run[e] above (in-order wave); the last lane of
+        // each id advances it for the next batch
+        __builtin_amdgcn_wave_barrier();
+        if (valid && rank == total - 1) run[e] += total;
+        __builtin_amdgcn_wave_barrier();
+      }
     }
 }
 
@@ -220,7 +251,7 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, 
     (void)topk;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
-    const size_t lds = sizeof(int32_t) * ((size_t)E * (3 + kWaves) + 1);
+    const size_t lds = sizeof(int32_t) * ((size_t)E * (2 + kWaves) + 1);
     const SmallQuant none = {};
     // work-groups 1.. quantize the small activation, one 16-element block per thread
     const int64_t qgroups = xq ? (xq->M * (xq->K / 16) + kRouteThreads - 1) / kRouteThreads : 0;
