@@ -163,6 +163,14 @@ __device__ __forceinline__ uint32_t quantize_block16(const uint32_t (&w)[8], con
     }
     const uint32_t code = e4m3_encode(s);
     const float den = e4m3_decode(code) * qs.gs;
+    // v = fl32(|x| / den), the IEEE float32 quotient, formed as
+    // fl32(fl64(|x| * r)) with r = fl64(1 / den) computed once per block.
+    // Exact: the quotient of two floats is never a float32 rounding midpoint
+    // and lies at least 2^-49 (relative) from one, while the float64 product
+    // is within 2^-52 of it, so both round to the same float32 (normal
+    // results; a subnormal quotient is far below the first E2M1 threshold
+    // either way, and an overflowing one is infinite either way).
+    const double rden = den > 0.0f ? 1.0 / (double)den : 0.0;
     uint32_t nib[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -171,7 +179,7 @@ __device__ __forceinline__ uint32_t quantize_block16(const uint32_t (&w)[8], con
             const uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
             uint32_t mag = 0;
             if (den > 0.0f) {
-                const float v = bf16_to_f32(b & 0x7FFFu) / den;
+                const float v = (float)((double)bf16_to_f32(b & 0x7FFFu) * rden);
                 mag = e2m1_magnitude(v);
             }
             nib[2 * i + h] = ((b >> 12) & 8u) | mag;

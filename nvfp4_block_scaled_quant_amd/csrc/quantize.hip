@@ -43,15 +43,23 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
                                                         uint32_t* __restrict__ slots) {
     const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)blockIdx.y * per);
     const int64_t nvec = per / 8;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
     uint32_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * kThreads) {
-        const u32x4 v = p[i];
+    // four independent 16-byte loads in flight per iteration
+    for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nvec; i0 += 4 * stride) {
+        u32x4 v[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            m = max(m, v[c] & 0x7FFFu);
-            m = max(m, (v[c] >> 16) & 0x7FFFu);
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            v[u] = i < nvec ? p[i] : (u32x4){0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                m = max(m, v[u][c] & 0x7FFFu);
+                m = max(m, (v[u][c] >> 16) & 0x7FFFu);
+            }
     }
     block_atomic_max(m, slots + blockIdx.y);
 }
