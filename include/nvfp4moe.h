@@ -33,12 +33,19 @@
  *                         row n is at
  *                           e * N * pitch_q(K) + (n / 16) * 16 * pitch_q(K)
  *                           + (kh / 64) * 1024 + (n % 16) * 64 + kh % 64
- *                w_sf_t   E * N * pitch_sf(K) E4M3 bytes, zero-padded, the same
- *                         blocking with 8-byte steps: scale g of row n is at
- *                           e * N * pitch_sf(K) + (n / 16) * 16 * pitch_sf(K)
- *                           + (g / 8) * 128 + (n % 16) * 8 + g % 8
- *   pitch_q(K)  = K/2 rounded up to a multiple of 64 bytes (a 128-element step)
- *   pitch_sf(K) = K/16 rounded up to a multiple of 8 bytes
+ *                w_sf_t   E * N * pitch_wsf(K) E4M3 bytes, zero-padded, in the
+ *                         same 16-row blocks, by groups of four K steps (st =
+ *                         g / 8 is the step of scale group g): scale g of row
+ *                         n is at
+ *                           e * N * pitch_wsf(K) + (n / 16) * 16 * pitch_wsf(K)
+ *                           + (st / 4) * 512 + (n % 16) * 32
+ *                           + ((g % 8) / 2) * 8 + (st % 4) * 2 + g % 2
+ *                         so the two groups of one 32-element quarter of a
+ *                         step sit together for four consecutive steps.
+ *   pitch_q(K)   = K/2 rounded up to a multiple of 64 bytes (a 128-element step)
+ *   pitch_sf(K)  = K/16 rounded up to a multiple of 8 bytes (activation scales)
+ *   pitch_wsf(K) = 32 bytes per group of four steps: pitch_q(K) / 64 rounded up
+ *                  to a multiple of 4, times 8
  *   The packed weights are the canonical ones with every matrix byte-transposed
  *   (the pages' GEMM took its weight operand column-major) and blocked so that
  *   one K step of 16 rows, the unit a matrix-core operand load covers, is one
@@ -129,9 +136,11 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N,
 /* ------------------------------------------------------------------------ *
  * nvfp4_operand_pitches - the padded row pitches of the packed weight layout
  * (and of the quantized operands inside the expert layer's workspace).
- *   K > 0, K % 16 == 0; ldq, ldsf: host int64 out (pitch_q(K), pitch_sf(K)).
+ *   K > 0, K % 16 == 0; ldq, ldsf, ldwsf: host int64 out (pitch_q(K),
+ *   pitch_sf(K), pitch_wsf(K)). Returns NVFP4_ESHAPE for K % 16 != 0 and
+ *   NVFP4_EINVAL for K <= 0 or a null pointer.
  * ------------------------------------------------------------------------ */
-int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf);
+int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf, int64_t* ldwsf);
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_prepack_weights - canonical (K-packed, N fastest) quantized weights to
@@ -139,7 +148,7 @@ int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf);
  * padding bytes written as zero). A pure data movement, no arithmetic.
  *
  *   w (E, K/2, N), w_sf (E, K/16, N): canonical bytes (nvfp4_quantize_weights)
- *   w_t (E * N * pitch_q(K) bytes), w_sf_t (E * N * pitch_sf(K) bytes): packed
+ *   w_t (E * N * pitch_q(K) bytes), w_sf_t (E * N * pitch_wsf(K) bytes): packed
  *   out, separate buffers (no in-place), w_t 16-byte and w_sf_t 8-byte aligned.
  *   K % 16 == 0, N % 16 == 0, E <= 65535. E == 0 is valid and enqueues nothing.
  * ------------------------------------------------------------------------ */
@@ -155,9 +164,9 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
  *   aq (M, K/2), asf (M, K/16): the quantized activation (nvfp4_quantize),
  *           aq 16-byte and asf 8-byte aligned
  *   a_gs    one float32, the activation's global scale
- *   bq (N * K/2 bytes), bsf (N * K/16 bytes): one packed weight matrix
- *           (nvfp4_prepack_weights with E = 1; for K % 128 == 0 the pitches
- *           are exactly K/2 and K/16), bq 16-byte and bsf 8-byte aligned
+ *   bq (N * K/2 bytes), bsf (N * pitch_wsf(K) bytes): one packed weight
+ *           matrix (nvfp4_prepack_weights with E = 1; for K % 128 == 0,
+ *           pitch_q(K) is exactly K/2), bq 16-byte and bsf 8-byte aligned
  *   b_alpha one float32
  *   out (M, N) bf16
  * Products of dequantized elements are exact; the sum is float32; the alpha
@@ -183,8 +192,8 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *   x             (T, H) bf16
  *   topk_ids      (T, topk) int32
  *   topk_weights  (T, topk) float32, used as given (no renormalization)
- *   w13 (E * 2I * pitch_q(H) bytes), w13_sf (E * 2I * pitch_sf(H)), w13_alpha (E)
- *   w2  (E * H * pitch_q(I) bytes),  w2_sf  (E * H * pitch_sf(I)),  w2_alpha  (E)
+ *   w13 (E * 2I * pitch_q(H) bytes), w13_sf (E * 2I * pitch_wsf(H)), w13_alpha (E)
+ *   w2  (E * H * pitch_q(I) bytes),  w2_sf  (E * H * pitch_wsf(I)),  w2_alpha  (E)
  *                 packed weights (nvfp4_prepack_weights of the canonical
  *                 (E, H/2, 2I) and (E, I/2, H) tensors); w13, w2 16-byte and
  *                 the scale tensors 8-byte aligned

@@ -6,7 +6,7 @@ mirror the C ABI in include/nvfp4moe.h:
 
     quantize(x)                      -> (q, sf, gs)
     quantize_weights(w)              -> (q, sf, alpha)    canonical weight layout
-    operand_pitches(K)               -> (ldq, ldsf)
+    operand_pitches(K)               -> (ldq, ldsf, ldwsf)
     packed_shapes(E, K, N)           -> shapes of the packed weight tensors
     prepack_weights(q, sf)           -> (q_t, sf_t)       packed layout the GEMMs read
     gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
@@ -40,7 +40,7 @@ _SIGS = {
     "nvfp4_quantize": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "nvfp4_quantize_weights_workspace": ([_i64, _i64, _i64], _sz),
     "nvfp4_quantize_weights": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
-    "nvfp4_operand_pitches": ([_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64)], _int),
+    "nvfp4_operand_pitches": ([_i64] + [ctypes.POINTER(_i64)] * 3, _int),
     "nvfp4_prepack_weights": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
     "nvfp4_gemm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
     "nvfp4_moe_workspace": ([_i64, _i64, _i64, _i64, _i64], _sz),
@@ -134,22 +134,25 @@ def quantize_weights(w):
 
 
 def operand_pitches(K):
-    """Row pitches (bytes) of the packed weight layout for reduction length K:
-    (K/2 rounded up to 64, K/16 rounded up to 8)."""
-    ldq, ldsf = _i64(), _i64()
-    _check(_lib.nvfp4_operand_pitches(K, ctypes.byref(ldq), ctypes.byref(ldsf)),
+    """Row pitches (bytes) for reduction length K: ldq (packed data, K/2
+    rounded up to 64), ldsf (activation scales, K/16 rounded up to 8), ldwsf
+    (packed weight scales, whole groups of four 128-element steps)."""
+    ldq, ldsf, ldwsf = _i64(), _i64(), _i64()
+    _check(_lib.nvfp4_operand_pitches(K, ctypes.byref(ldq), ctypes.byref(ldsf), ctypes.byref(ldwsf)),
            "nvfp4_operand_pitches")
-    return ldq.value, ldsf.value
+    return ldq.value, ldsf.value, ldwsf.value
 
 
 def packed_shapes(E, K, N):
-    """Shapes of the packed weight tensors of E matrices (K, N): 16-row blocks
-    of one 128-element K step each, (E, N/16, steps, 16, 64) data bytes and
-    (E, N/16, steps, 16, 8) scale bytes, steps = pitch_q(K) / 64."""
-    ldq, ldsf = operand_pitches(K)
+    """Shapes of the packed weight tensors of E matrices (K, N), in 16-row
+    blocks: data (E, N/16, steps, 16, 64), one 128-element K step of the
+    block's 16 rows after another, steps = ldq / 64; scales (E, N/16, quads,
+    16, 32), quads = ldwsf / 32: per group of four K steps, row, pair of scale
+    groups (4), step of the four (4), then the pair's two bytes."""
+    ldq, _, ldwsf = operand_pitches(K)
     if N % 16:
         raise ValueError("packed weights need N % 16 == 0")
-    return (E, N // 16, ldq // 64, 16, 64), (E, N // 16, ldsf // 8, 16, 8)
+    return (E, N // 16, ldq // 64, 16, 64), (E, N // 16, ldwsf // 32, 16, 32)
 
 
 def prepack_weights(q, sf):
@@ -171,8 +174,8 @@ def prepack_weights(q, sf):
 
 def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
     """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times one
-    packed weight matrix bq (N/16, K/128, 16, 64) + bsf (N/16, K/128, 16, 8)
-    -> bf16 (M, N). K % 128 == 0."""
+    packed weight matrix bq (N/16, K/128, 16, 64) + bsf (N/16, quads, 16, 32)
+    (packed_shapes with E dropped) -> bf16 (M, N). K % 128 == 0."""
     for t, n, d in ((aq, "aq", torch.uint8), (asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
                     (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
                     (b_alpha, "b_alpha", torch.float32)):
@@ -183,7 +186,7 @@ def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
     K = aq.shape[1] * 2
     N = bq.shape[0] * 16
     if (K % 128 or tuple(bq.shape) != (N // 16, K // 128, 16, 64) or asf.shape != (M, K // 16)
-            or tuple(bsf.shape) != (N // 16, K // 128, 16, 8)):
+            or tuple(bsf.shape) != packed_shapes(1, K, N)[1][1:]):
         raise ValueError("operand shapes do not match")
     out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device) if out is None else out
     _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),

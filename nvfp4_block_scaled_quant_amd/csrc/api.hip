@@ -108,7 +108,7 @@ const char* nvfp4_strerror(int status) {
     }
 }
 
-int nvfp4_version(void) { return (2 << 16) | 0; }
+int nvfp4_version(void) { return (3 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -163,12 +163,13 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N, u
 }
 
 // ---------------------------------------------------------------------------
-int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf) {
+int nvfp4_operand_pitches(int64_t K, int64_t* ldq, int64_t* ldsf, int64_t* ldwsf) {
     if (K <= 0) return NVFP4_EINVAL;
     if (K % 16) return NVFP4_ESHAPE;
-    if (!ldq || !ldsf) return NVFP4_EINVAL;
+    if (!ldq || !ldsf || !ldwsf) return NVFP4_EINVAL;
     *ldq = pitch_q(K);
     *ldsf = pitch_sf(K);
+    *ldwsf = pitch_wsf(K);
     return NVFP4_OK;
 }
 
@@ -181,8 +182,8 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
     if (!aligned(w_t, 16) || !aligned(w_sf_t, 8)) return NVFP4_EINVAL;
     int dv = check_device();
     if (dv) return dv;
-    NVFP4_TRY(launch_pack_weights(w, E, K / 2, N, w_t, pitch_q(K), 64, stream));
-    NVFP4_TRY(launch_pack_weights(w_sf, E, K / 16, N, w_sf_t, pitch_sf(K), 8, stream));
+    NVFP4_TRY(launch_pack_weights(w, E, K / 2, N, w_t, pitch_q(K), false, stream));
+    NVFP4_TRY(launch_pack_weights(w_sf, E, K / 16, N, w_sf_t, pitch_wsf(K), true, stream));
     return NVFP4_OK;
 }
 

@@ -17,12 +17,15 @@
 // alongside; B comes in 16-row blocks whose K steps are contiguous (1 KB per
 // step), so every load instruction of B reads one contiguous kilobyte. Tiles
 // move from HBM to LDS by buffer loads that write LDS directly (no staging
-// registers; out-of-range offsets read zeros), four stages deep (36 KB each).
+// registers; out-of-range offsets read zeros), four stages deep (38 KB each).
 //
 // LDS layout. A stage holds 256 A rows and 256 B rows of 64 bytes, unpadded;
 // the four 16-byte chunks of a row are XOR-swizzled with bits 2-3 of the row,
 // so that the 16 rows read by a 16-lane group of the fragment loads cover all
-// banks. Scales: 8 bytes per row.
+// banks. Scales: 8 bytes per A row; per B row four dwords, one per pair of
+// scale groups (the packed weights store a pair of groups of four consecutive
+// K steps together, so a step's pairs are 2-byte pieces, and each is brought
+// in by a 2-byte load that fills a whole LDS dword, zero-extended).
 //
 // Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
 // 128 x 128 quadrant (4 x 4 tiles of 32 x 32 x 16). Lane l serves row / column
@@ -58,9 +61,9 @@ constexpr int NSTAGE = 4;
 constexpr int A_BYTES = BM * KB;       // 16 KB
 constexpr int B_BYTES = BN * KB;
 constexpr int ASF_BYTES = BM * 8;      // 2 KB
-constexpr int BSF_BYTES = BN * 8;
+constexpr int BSF_BYTES = BN * 16;     // 4 KB: one dword per scale pair
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES + ASF_BYTES + BSF_BYTES;
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 144 KB
+constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 152 KB
 constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw buffer, 32-bit data format
 
 // Work-group barrier for the main loop. __syncthreads() (and any workgroup
@@ -91,7 +94,8 @@ void gemm_kernel(GemmParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int64_t K = p.K, N = p.N;
-    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);      // padded row pitches
+    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);      // padded row pitches (A)
+    const int64_t ldwsf = pitch_wsf(K);                       // packed weight scales
     const int ntn = (MODE == kGemmL1) ? (int)((p.I + 127) / 128) : (int)((N + BN - 1) / BN);
     const int tile_idx = blockIdx.x / ntn;
     const int nt = blockIdx.x - tile_idx * ntn;
@@ -114,7 +118,7 @@ void gemm_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aq, p.a_rows * ldq);
     const __amdgpu_buffer_rsrc_t rasf = make_rsrc(p.asf, p.a_rows * ldsf);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
-    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldsf, N * ldsf);
+    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldwsf, N * ldwsf);
 
     auto a_src = [&](int r) -> int64_t {        // A tensor row of tile row r
         int64_t src = row_start + (r < row_count ? r : 0);
@@ -141,24 +145,28 @@ void gemm_kernel(GemmParams p) {
         a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
         b_off[t] = (uint32_t)(wq_row(b_src(row), ldq) + 16 * chunk);
     }
-    // scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 + lane:
-    // row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the step's 8
-    uint32_t asf_off[2], bsf_off[2];
+    // A scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 +
+    // lane: row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the
+    // step's 8. B scales: instruction t (0..3) fills dword (4w + t) * 64 + lane
+    // with pair lane & 3 of row (4w + t) * 16 + lane / 4.
+    uint32_t asf_off[2], bsf_off[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int row = (2 * wave + t) * 32 + (lane >> 1);
         asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
-        bsf_off[t] = (uint32_t)(wsf_row(b_src(row), ldsf) + 4 * (lane & 1));
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        bsf_off[t] = (uint32_t)wsf_off(b_src((4 * wave + t) * 16 + (lane >> 2)), ldwsf, 0, lane & 3);
 
     const int nk = (int)(ldq / KB);
     // part t (0..5) of the DMA of stage ks: t < 4 one A and one B data load,
-    // t = 4, 5 one A and one B scale load
+    // t = 4, 5 one A and two B scale loads
     auto issue_part = [&](int ks, int t) {
         uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
         // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
         const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
-        const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)ks * kWsfStep;
+        const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)((ks >> 2) * kWsfQuad + (ks & 3) * 2);
         if (t < 4) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
                                                      16, a_off[t], kda, 0, 0);
@@ -168,9 +176,11 @@ void gemm_kernel(GemmParams p) {
             const int u = t - 4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + u) * 256), 4, asf_off[u], ksa, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (2 * wave + u) * 256), 4,
-                bsf_off[u], ksb, 0, 0);
+#pragma unroll
+            for (int v = 2 * u; v < 2 * u + 2; ++v)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (4 * wave + v) * 256), 2,
+                    bsf_off[v], ksb, 0, 0);
         }
     };
     auto issue_stage = [&](int ks) {
@@ -210,7 +220,9 @@ void gemm_kernel(GemmParams p) {
             const int vc = wn * 128 + 32 * j + l32;
             fb[j][0] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h));
             fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
-            sb[j] = *reinterpret_cast<const uint32_t*>(sBsf + vc * 8 + 4 * h);
+            // pairs 2h and 2h + 1, each in the low half of its dword
+            const u32x2 d = *reinterpret_cast<const u32x2*>(sBsf + vc * 16 + 8 * h);
+            sb[j] = d[0] | (d[1] << 16);
         }
     };
     // operands of substep s in registers s & 1
@@ -238,9 +250,9 @@ void gemm_kernel(GemmParams p) {
     read_frags(0);
     deq(0, ha[0], hb[0]);
 
-    // One K step. Phase 0: steady state (refill a stage, wait until 24 loads
+    // One K step. Phase 0: steady state (refill a stage, wait until 28 loads
     // remain, fetch the next step); 1 and 2: the last two refills have been
-    // issued (wait until 12 / 0 remain); 3: the last step. Every condition is a
+    // issued (wait until 14 / 0 remain); 3: the last step. Every condition is a
     // compile-time constant, so a step is one basic block the scheduler can
     // interleave freely.
     auto step = [&](int ks, auto mode_c) {
@@ -248,7 +260,7 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             // the refill of stage ks+3 is spread over substeps 0..5: a burst of
-            // twelve LDS-DMA issues at once stalls the MFMA stream
+            // fourteen LDS-DMA issues at once stalls the MFMA stream
             if (PH == 0 && s < 6) issue_part(ks + NSTAGE - 1, s);
             if (s < 7) {
                 deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
@@ -256,8 +268,8 @@ void gemm_kernel(GemmParams p) {
                 // this wave's DMA of stage ks+1 is done when at most the stages
                 // issued after it are outstanding; lgkmcnt(0): its own fragment
                 // reads of this step are complete before it passes the barrier
-                if (PH == 0) __builtin_amdgcn_s_waitcnt(0x4078);        // vmcnt(24) lgkmcnt(0)
-                if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007C);        // vmcnt(12) lgkmcnt(0)
+                if (PH == 0) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
+                if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007E);        // vmcnt(14) lgkmcnt(0)
                 if (PH == 2) __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
                 lds_barrier();
                 read_frags(ks + 1);

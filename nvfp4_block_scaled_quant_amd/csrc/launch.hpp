@@ -47,19 +47,28 @@ __host__ __device__ inline int64_t pitch_sf(int64_t K) { return (K / 16 + 7) / 8
 // Packed weight layout. A weight matrix is N rows (one per output column) of
 // pitch_q(K) bytes, K-packed; rows are grouped in blocks of 16, and inside a
 // block the 64 bytes of one 128-element K step of all 16 rows are stored
-// together (1 KB), step after step. Scales likewise: 8 bytes per row and step,
-// 128 bytes per block and step. So one K step of a 16-row block, the unit an
-// MFMA operand load covers, is contiguous.
+// together (1 KB), step after step. So one K step of a 16-row block, the unit
+// an MFMA operand load covers, is contiguous.
+// Scales: per block, groups of four K steps (512 bytes): row c (0..15), pair q
+// (0..3: groups 2q, 2q+1 of a step), step u of the four, then the two bytes.
+// The two scale bytes a streaming lane needs for four consecutive steps are
+// thus one 8-byte piece, and a wave reads 512 contiguous bytes at once.
 constexpr int kWqStep = 16 * 64;      // bytes of one K step of a 16-row block
-constexpr int kWsfStep = 16 * 8;
+constexpr int kWsfQuad = 16 * 32;     // scale bytes of four K steps of a block
 __host__ __device__ inline int64_t wq_row(int64_t n, int64_t ldq) { return (n >> 4) * 16 * ldq + (n & 15) * 64; }
-__host__ __device__ inline int64_t wsf_row(int64_t n, int64_t ldsf) { return (n >> 4) * 16 * ldsf + (n & 15) * 8; }
+// scale row pitch of the packed weights: whole groups of four K steps
+__host__ __device__ inline int64_t pitch_wsf(int64_t K) { return (pitch_q(K) / 64 + 3) / 4 * 32; }
+// offset of scale pair q of K step st of row n (two bytes: groups 8st + 2q, +1)
+__host__ __device__ inline int64_t wsf_off(int64_t n, int64_t ldsf, int64_t st, int q) {
+    return (n >> 4) * 16 * ldsf + (st >> 2) * kWsfQuad + (n & 15) * 32 + q * 8 + (st & 3) * 2;
+}
 
 // Canonical (R, C) byte matrices (E of them, R = K-packed rows, C = N) into
 // the packed layout: element (r, c) goes to row c, byte r of a row of pitch
-// ldo, in steps of sw bytes (64 for data, 8 for scales); padding bytes are 0.
+// ldo; scales (scale_layout) in the four-step groups above, data in steps of
+// 64 bytes. Padding bytes are 0.
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
-                               int64_t ldo, int sw, hipStream_t s);
+                               int64_t ldo, bool scale_layout, hipStream_t s);
 
 // Column-block quantization of E weight matrices (E, K, N) with per-matrix amax.
 hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
@@ -103,7 +112,7 @@ struct GemmParams {
     const int32_t* a_gather;   // L1: sorted row -> slot index; token = slot / topk
     int topk;
     // B: per-expert weights, one K-packed row per output column (N rows of
-    // pitch_q(K) bytes, scales N rows of pitch_sf(K) bytes)
+    // pitch_q(K) bytes, scales N rows of pitch_wsf(K) bytes, packed layout)
     const uint8_t* bq;
     const uint8_t* bsf;
     int64_t N;                 // columns of B

@@ -81,10 +81,11 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
 }
 
 // Canonical (R, C) byte matrices -> the packed weight layout (launch.hpp),
-// through a 64 x 64 LDS tile: reads along C and writes along R are coalesced.
+// through a 64 x 64 LDS tile: reads along C are coalesced, writes land in
+// 64-byte runs (data) or 2-byte pieces (scales).
 __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
     const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out, int64_t ldo,
-    int sw) {
+    int scale_layout) {
     __shared__ uint8_t tile[64][65];
     const int64_t e = blockIdx.z;
     const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -99,8 +100,11 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
     for (int i = threadIdx.x; i < 64 * 64; i += kThreads) {
         const int cc = i >> 6, rr = i & 63;
         const int64_t r = r0 + rr, c = c0 + cc;
-        if (c < C && r < ldo)
-            dst[(c >> 4) * 16 * ldo + (r / sw) * 16 * sw + (c & 15) * sw + r % sw] = tile[rr][cc];
+        if (c < C && r < ldo) {
+            const int64_t o = scale_layout ? wsf_off(c, ldo, r >> 3, (int)((r & 7) >> 1)) + (r & 1)
+                                           : (c >> 4) * 16 * ldo + (r >> 6) * kWqStep + (c & 15) * 64 + (r & 63);
+            dst[o] = tile[rr][cc];
+        }
     }
 }
 
@@ -176,12 +180,12 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int3
 }
 
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
-                               int64_t ldo, int sw, hipStream_t s) {
+                               int64_t ldo, bool scale_layout, hipStream_t s) {
     if (E <= 0 || C <= 0) return hipSuccess;
     // rows of the output beyond R (padding) are covered by extra row tiles
     const int64_t rt = (ldo + 63) / 64, ct = (C + 63) / 64;
-    pack_weights_kernel<<<dim3((unsigned)ct, (unsigned)rt, (unsigned)E), kThreads, 0, s>>>(in, R, C, out, ldo,
-                                                                                        sw);
+    pack_weights_kernel<<<dim3((unsigned)ct, (unsigned)rt, (unsigned)E), kThreads, 0, s>>>(
+        in, R, C, out, ldo, scale_layout ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -22,12 +22,19 @@
 //   substep s (K values 32q + 8s .. +8 of the step); A rows are read from LDS
 //   with the same K permutation, so every k meets its own partner. Nothing of
 //   B goes through LDS.
+// * The packed weight scales keep the two scale bytes a lane needs per step
+//   together for four consecutive steps (8 bytes; a wave's 64 lanes read 512
+//   contiguous bytes), so scales are loaded only with the first step of each
+//   group of four (and with the first step a wave streams, which may fall
+//   inside a group) and are kept in registers for the group's other steps.
 // * Dequantization is exact (E2M1 x E4M3 in f16, see common.hpp); the
 //   epilogue applies alpha once (and for L1 the bf16 roundings and SiLU).
 //
 // For L1, blocks f < 4 are gate columns 16f + c of the wave's 64 and blocks
 // f + 4 the matching up columns, so gate and up of one output column sit in
 // the same lane and accumulator position.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -43,7 +50,7 @@ constexpr int WROWS = 16 * NB;    // weight rows per wave
 constexpr int GB = NB / 2;        // L1: gate blocks (and as many up blocks) per wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr int kStreamNT = 2;      // buffer-load cache policy: non-temporal (read once)
-constexpr int kStagger = 13;      // start-step offset between consecutive waves
+constexpr int kStagger = 13;      // start offset (in groups of four K steps) between waves
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
@@ -62,7 +69,7 @@ void skinny_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t K = p.K, N = p.N, Kg = K / 16;
-    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);
+    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K), ldwsf = pitch_wsf(K);
     const int nslab = (int)skinny_slabs(MODE, p.I, N);
     const int tile_idx = blockIdx.x / nslab;
     const int slab = blockIdx.x - tile_idx * nslab;
@@ -77,7 +84,7 @@ void skinny_kernel(GemmParams p) {
     // ---- this lane's NB weight rows -------------------------------------------
     const int c = lane & 15, q = lane >> 4;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
-    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldsf, N * ldsf);
+    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldwsf, N * ldwsf);
     // first output column of this wave: L1 act column, L2 weight row
     const int64_t col0 = (MODE == kGemmL1) ? ((int64_t)slab * NW + wave) * 16 * GB
                                            : ((int64_t)slab * NW + wave) * WROWS;
@@ -96,53 +103,71 @@ void skinny_kernel(GemmParams p) {
             row = ok[f] ? row : 0;
         }
         boff[f] = (uint32_t)(wq_row(row, ldq) + 16 * q);
-        sfoff[f] = (uint32_t)(wsf_row(row, ldsf) + 2 * q);
+        sfoff[f] = (uint32_t)wsf_off(row, ldwsf, 0, q);
     }
     // a wave whose columns all lie beyond the matrix streams nothing
     const bool active = (MODE == kGemmL1) ? (col0 < p.I) : (col0 < N);
     const int nsteps = active ? (int)(ldq / 64) : 0;
     // Waves start at different K steps and wrap around, so that at any moment
     // the concurrent streams spread over the memory channels instead of all
-    // starting at the same offset of their blocks. The order of the fp32
-    // partial sums is fixed per output column.
-    const int s0 = nsteps ? (int)(((int64_t)blockIdx.x * NW + wave) * kStagger % nsteps) : 0;
+    // starting at the same offset of their blocks. Starts are whole groups of
+    // four steps (when K has whole groups; else every wave starts at 0), so
+    // that loop step i begins a scale group exactly when i % 4 == 0. The
+    // order of the fp32 partial sums is fixed per output column.
+    const int ngroups = nsteps / 4;
+    const int s0 = (nsteps % 4 == 0 && ngroups)
+                       ? 4 * (int)(((int64_t)blockIdx.x * NW + wave) * kStagger % ngroups) : 0;
     auto kstep = [&](int i) { return i + s0 < nsteps ? i + s0 : i + s0 - nsteps; };
 
     struct Raw {
         u32x4 w[NB];
-        uint32_t s[NB];
+        u32x2 s[NB];      // scales of four steps, loaded with the group's first step
     };
-    auto load = [&](int i, Raw& rw) {
+    // Loop step i with i % 4 == 0 brings (and uses) a new group of scales. `ng`
+    // is that condition, a compile-time constant in the steady-state loop:
+    // there every iteration issues the same loads, so the compiler's waits
+    // for a step's registers let the next step's loads stay in flight.
+    auto load = [&](int i, Raw& rw, auto ng) {
         // the step offsets go to the scalar offset operand: keep them uniform
         const int st = kstep(i);
         const uint32_t kd = __builtin_amdgcn_readfirstlane((uint32_t)st * kWqStep);
-        const uint32_t ksf = __builtin_amdgcn_readfirstlane((uint32_t)st * kWsfStep);
+        if (ng) {
+            const uint32_t ksf = __builtin_amdgcn_readfirstlane((uint32_t)(st >> 2) * kWsfQuad);
 #pragma unroll
-        for (int f = 0; f < NB; ++f) {
-            rw.w[f] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[f], kd, kStreamNT);
-            rw.s[f] = __builtin_amdgcn_raw_buffer_load_b16(rbsf, sfoff[f], ksf, kStreamNT);
+            for (int f = 0; f < NB; ++f)
+                rw.s[f] = __builtin_amdgcn_raw_buffer_load_b64(rbsf, sfoff[f], ksf, kStreamNT);
         }
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+            rw.w[f] = __builtin_amdgcn_raw_buffer_load_b128(rb, boff[f], kd, kStreamNT);
     };
+    const std::true_type kNew;
+    const std::false_type kOld;
 
-    // the first two weight steps are in flight while A is staged
+    // A tensor row of each tile row (-1: none), read before the weight loads
+    // below are issued, so that waiting for it does not wait for them
+    int64_t my_src = -1;
+    if (tid < SM && tid < row_count) {
+        my_src = row_start + tid;
+        if (MODE == kGemmL1) my_src = p.a_gather[my_src] / p.topk;
+    }
+
+    // The first two weight steps are in flight while A is staged. Both loads
+    // are issued on every path into the main loop, in this order (a wave with
+    // fewer steps loads step 0 again), so that the compiler's waits at the
+    // loop head are the ones of the steady state.
     Raw r0, r1;
-    int st = 0;
-    if (st < nsteps) load(st, r0);
-    if (st + 1 < nsteps) load(st + 1, r1);
+    load(0, r0, kNew);
+    __builtin_amdgcn_sched_barrier(0);
+    load(nsteps > 1 ? 1 : 0, r1, kOld);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- stage the tile's A rows (packed, pitch ldq) and scales into LDS ------
     uint8_t* sA = smem;                              // [16][ldq + 16]
     const int a_pitch = (int)ldq + 16;               // 16-byte skew between rows
     uint8_t* sAsf = smem + SM * a_pitch;             // [16][ldsf]
-    __shared__ int64_t src_row[SM];                  // A tensor row of each tile row, -1: none
-    if (tid < SM) {
-        int64_t src = -1;
-        if (tid < row_count) {
-            src = row_start + tid;
-            if (MODE == kGemmL1) src = p.a_gather[src] / p.topk;
-        }
-        src_row[tid] = src;
-    }
+    __shared__ int64_t src_row[SM];
+    if (tid < SM) src_row[tid] = my_src;
     __syncthreads();
     {
         // scales: 8-byte pieces (groups beyond K are masked in compute())
@@ -189,8 +214,10 @@ void skinny_kernel(GemmParams p) {
     float4_t acc[NB];
 #pragma unroll
     for (int f = 0; f < NB; ++f) acc[f] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // scales of the current group; the low 16 bits belong to the step at hand
+    uint64_t cur[NB];
 
-    auto compute = [&](int i, const Raw& rw) {
+    auto compute = [&](int i, const Raw& rw, auto ng) {
         const int st = kstep(i);
         // A row c, bytes [16q, 16q + 16) of the step; scale groups 2q, 2q + 1
         const u32x4 aw = *reinterpret_cast<const u32x4*>(sA + c * a_pitch + st * 64 + 16 * q);
@@ -200,27 +227,53 @@ void skinny_kernel(GemmParams p) {
         const int64_t g0 = (int64_t)st * 8 + 2 * q;
         const uint32_t mask = (g0 < Kg ? 0xFFu : 0u) | (g0 + 1 < Kg ? 0xFF00u : 0u);
         as &= mask;
+        if (ng) {
+#pragma unroll
+            for (int f = 0; f < NB; ++f) cur[f] = ((uint64_t)rw.s[f][1] << 32) | rw.s[f][0];
+        }
+        // B scales of groups beyond K are zero in the packed layout
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const half8_t ha = dequant8(aw[s], scale_pair((as >> (8 * (s >> 1))) & 0xFFu));
 #pragma unroll
             for (int f = 0; f < NB; ++f) {
-                const uint32_t code = ((rw.s[f] & mask) >> (8 * (s >> 1))) & 0xFFu;
+                const uint32_t code = ((uint32_t)cur[f] >> (8 * (s >> 1))) & 0xFFu;
                 const half8_t hb = dequant8(rw.w[f][s], scale_pair(code));
                 acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha, hb, acc[f], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int f = 0; f < NB; ++f) cur[f] >>= 16;
     };
 
-    // two steps in flight: r0 holds loop step st, r1 step st + 1
-    while (st < nsteps) {
-        compute(st, r0);
-        ++st;
-        if (st >= nsteps) break;
-        if (st + 1 < nsteps) load(st + 1, r0);
-        compute(st, r1);
-        ++st;
-        if (st + 1 < nsteps) load(st + 1, r1);
+    // Two steps in flight: r0 holds the even loop steps, r1 the odd ones. The
+    // steady-state loop covers four steps per iteration (one scale group);
+    // the last at most five steps run through the general loop below.
+    // Scheduling barriers keep each step's MFMAs (and so the waits for its
+    // registers) from being hoisted into the step before.
+    int i = 0;
+    for (; i + 5 < nsteps; i += 4) {
+        compute(i, r0, kNew);
+        load(i + 2, r0, kOld);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 1, r1, kOld);
+        load(i + 3, r1, kOld);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 2, r0, kOld);
+        load(i + 4, r0, kNew);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(i + 3, r1, kOld);
+        load(i + 5, r1, kOld);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    while (i < nsteps) {
+        compute(i, r0, (i & 3) == 0);
+        ++i;
+        if (i >= nsteps) break;
+        if (i + 1 < nsteps) load(i + 1, r0, (i & 3) == 3);
+        compute(i, r1, (i & 3) == 0);
+        ++i;
+        if (i + 1 < nsteps) load(i + 1, r1, (i & 3) == 3);
     }
 
     // ---- epilogue: acc[f][i] = D[tile row 4q + i][column c of block f] --------

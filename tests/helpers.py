@@ -161,8 +161,8 @@ def run_gpu_layer(nv, L, repeat=1, packed=None):
     lay = nv.moe_workspace_layout(T, H, I, E, k)
     wsh = ws.cpu().numpy()
     S = T * k
-    ldq_h, ldsf_h = nv.operand_pitches(H)
-    ldq_i, ldsf_i = nv.operand_pitches(I)
+    ldq_h, ldsf_h, _ = nv.operand_pitches(H)
+    ldq_i, ldsf_i, _ = nv.operand_pitches(I)
 
     def view(name, dtype, count):
         o = lay[name]

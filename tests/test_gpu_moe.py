@@ -120,10 +120,14 @@ def test_ragged_shapes(nv, T, H, I, E, k):
 
 
 # shapes where slots per expert average at most 16 take the weight-streaming
-# path (16-row tiles): single rows, experts spanning several tiles, K tails
+# path (16-row tiles): single rows, experts spanning several tiles, K tails;
+# K of 8, 12 and 16 whole 128-element steps (two to four groups of four:
+# waves start at different groups and wrap around) and of 6 and 9 steps
+# (a partial last group)
 @pytest.mark.parametrize("T,H,I,E,k", [(8, 256, 128, 8, 4), (60, 512, 256, 8, 2),
                                        (20, 272, 144, 4, 2), (3, 1040, 400, 16, 5),
-                                       (33, 128, 16, 3, 1)])
+                                       (33, 128, 16, 3, 1), (12, 1024, 1536, 8, 2),
+                                       (5, 2048, 768, 6, 3)])
 def test_small_batch_shapes(nv, T, H, I, E, k):
     assert T * k <= 16 * E
     cfg = W.small_layer(f"s{T}", T=T, H=H, I=I, E=E, topk=k, seed=3 * T + H + I)

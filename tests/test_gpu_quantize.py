@@ -114,13 +114,27 @@ def test_quantize_weights_full_expert(nv):
         assert (q[0] == rq).all()
 
 
-def _packed_layout(a, pitch, sw):
-    # canonical (E, R, C) -> rows of C, padded to `pitch` bytes, in 16-row
-    # blocks whose `sw`-byte K steps are stored together
+def _padded_rows(a, pitch):
+    # canonical (E, R, C) -> C rows of `pitch` bytes each, zero padded
     E, R, C = a.shape
     rows = np.zeros((E, C, pitch), np.uint8)
     rows[:, :, :R] = a.transpose(0, 2, 1)
-    return rows.reshape(E, C // 16, 16, pitch // sw, sw).transpose(0, 1, 3, 2, 4)
+    return rows
+
+
+def _packed_data(q, ldq):
+    # 16-row blocks whose 64-byte K steps are stored together
+    E, _, C = q.shape
+    return _padded_rows(q, ldq).reshape(E, C // 16, 16, ldq // 64, 64).transpose(0, 1, 3, 2, 4)
+
+
+def _packed_scales(sf, ldwsf):
+    # a row's scale groups g = 32 quad + 8 u + 2 pair + b (step 4 quad + u of
+    # the quad, pair of groups, byte) are stored per 16-row block as
+    # [quad][row][pair][u][b]
+    E, _, C = sf.shape
+    rows = _padded_rows(sf, ldwsf).reshape(E, C // 16, 16, ldwsf // 32, 4, 4, 2)
+    return rows.transpose(0, 1, 3, 2, 5, 4, 6).reshape(E, C // 16, ldwsf // 32, 16, 32)
 
 
 @pytest.mark.parametrize("E,K,N", [(1, 16, 16), (3, 272, 48), (2, 256, 208), (1, 7168, 96),
@@ -132,8 +146,14 @@ def test_prepack_weights_layout(nv, E, K, N):
     q = rng.integers(0, 256, (E, K // 2, N)).astype(np.uint8)
     sf = rng.integers(0, 256, (E, K // 16, N)).astype(np.uint8)
     q_t, sf_t = (to_host(t) for t in nv.prepack_weights(to_dev(q), to_dev(sf)))
-    ldq, ldsf = nv.operand_pitches(K)
+    ldq, _, ldwsf = nv.operand_pitches(K)
     assert q_t.shape == (E, N // 16, ldq // 64, 16, 64)
-    assert sf_t.shape == (E, N // 16, ldsf // 8, 16, 8)
-    assert (q_t == _packed_layout(q, ldq, 64)).all()
-    assert (sf_t == _packed_layout(sf, ldsf, 8)).all()
+    assert sf_t.shape == (E, N // 16, ldwsf // 32, 16, 32)
+    assert (q_t == _packed_data(q, ldq)).all()
+    assert (sf_t == _packed_scales(sf, ldwsf)).all()
+    # spot checks of the scale layout by its index formula
+    for e, g, c in [(0, 0, 0), (E - 1, K // 16 - 1, N - 1), (0, min(9, K // 16 - 1), min(17, N - 1))]:
+        st, pair, b = g // 8, (g % 8) // 2, g % 2
+        flat = sf_t[e].reshape(-1)
+        off = (c // 16) * 16 * ldwsf + (st // 4) * 512 + (c % 16) * 32 + pair * 8 + (st % 4) * 2 + b
+        assert flat[off] == sf[e, g, c]

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (2, 0)
+    assert nv.version() == (3, 0)
     for code in range(6):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
@@ -97,14 +97,18 @@ def test_gemm_argument_errors(nv):
 
 
 def test_operand_pitches(nv):
-    for K, want in [(16, (64, 8)), (128, (64, 8)), (144, (128, 16)), (272, (192, 24)),
-                    (7168, (3584, 448)), (3072, (1536, 192)), (400, (256, 32))]:
+    # (ldq, ldsf, ldwsf): data in whole 128-element steps, activation scales
+    # in whole 8-byte steps, packed weight scales in whole groups of four steps
+    for K, want in [(16, (64, 8, 32)), (128, (64, 8, 32)), (144, (128, 16, 32)),
+                    (272, (192, 24, 32)), (7168, (3584, 448, 448)), (3072, (1536, 192, 192)),
+                    (400, (256, 32, 32)), (640, (320, 40, 64))]:
         assert nv.operand_pitches(K) == want
-    ldq, ldsf = ctypes.c_int64(), ctypes.c_int64()
+    ldq, ldsf, ldw = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     f = lib(nv).nvfp4_operand_pitches
-    assert f(24, ctypes.byref(ldq), ctypes.byref(ldsf)) == 2
-    assert f(0, ctypes.byref(ldq), ctypes.byref(ldsf)) == 1
-    assert f(32, None, ctypes.byref(ldsf)) == 1
+    assert f(24, ctypes.byref(ldq), ctypes.byref(ldsf), ctypes.byref(ldw)) == 2
+    assert f(0, ctypes.byref(ldq), ctypes.byref(ldsf), ctypes.byref(ldw)) == 1
+    assert f(32, None, ctypes.byref(ldsf), ctypes.byref(ldw)) == 1
+    assert f(32, ctypes.byref(ldq), ctypes.byref(ldsf), None) == 1
 
 
 def test_prepack_argument_errors(nv):
@@ -145,8 +149,8 @@ def test_moe_workspace_layout_is_consistent(nv):
         total = nv.moe_workspace_size(*shape)
         lay = nv.moe_workspace_layout(*shape)
         S = T * k
-        qh, sh = nv.operand_pitches(H)
-        qi, si = nv.operand_pitches(I)
+        qh, sh, _ = nv.operand_pitches(H)
+        qi, si, _ = nv.operand_pitches(I)
         ends = {"xq": T * qh, "xsf": T * sh, "gs1": 4, "gs2": 4, "counts": 4 * E,
                 "offsets": 4 * (E + 1), "sorted_slot": 4 * S, "slot_row": 4 * S,
                 "act": 2 * S * I, "aq": S * qi, "asf": S * si, "o2": 4 * S * H}
