@@ -120,16 +120,19 @@ E4M3_POS = [e4m3_value(c) for c in range(127)]
 E2M1_POS = [e2m1_value(n) for n in range(8)]
 
 
-def quantize(rows_bits):
+def quantize(rows_bits, gs=None):
     """Quantize rows of bf16 bit patterns, blocks of 16 along each row.
 
+    gs: None for the tensor's own global scale fl32(amax / 2688), or a given
+    (static) float32 global scale.
     Returns (q rows of bytes, sf rows of bytes, gs as a float).
     """
     ncols = len(rows_bits[0]) if rows_bits else 0
     assert ncols % 16 == 0
     rows = [[bf16_value(b) for b in r] for r in rows_bits]
-    amax = max((abs(Fraction(v)) for r in rows for v in r), default=Fraction(0))
-    gs = f32(amax / 2688)
+    if gs is None:
+        amax = max((abs(Fraction(v)) for r in rows for v in r), default=Fraction(0))
+        gs = f32(amax / 2688)
     six_gs = f32(6 * Fraction(gs))
     q_rows, sf_rows = [], []
     for r in rows:

@@ -32,7 +32,7 @@ import numpy as np
 
 from .formats import bf16_from_f64, bf16_to_f32
 from .quantize import (dequantize_cols, dequantize_rows, quantize_bf16,
-                       quantize_f32)
+                       quantize_bf16_static, quantize_f32)
 
 
 def silu(z):
@@ -57,7 +57,10 @@ def _l1_expert(task):
     xq_rows, xsf_rows, w13q_e, w13sf_e, alpha, I, keep = task
     a = dequantize_rows(xq_rows, xsf_rows)
     b = dequantize_cols(w13q_e, w13sf_e)
-    gu_f64 = alpha * (a @ b)
+    ab = a @ b
+    # alpha: one value for all 2I columns, or (gate, up) one per half
+    ag, au = (alpha, alpha) if np.ndim(alpha) == 0 else (alpha[0], alpha[1])
+    gu_f64 = np.concatenate([ag * ab[:, :I], au * ab[:, I:]], axis=1)
     gu = bf16_from_f64(gu_f64)                                       # R1
     g = bf16_to_f32(gu[:, :I]).astype(np.float64)
     u = bf16_to_f32(gu[:, I:]).astype(np.float64)
@@ -78,12 +81,17 @@ def _map(fn, tasks, pool):
 
 
 def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
-                w2q, w2sf, w2_alpha, keep=False, pool=None):
+                w2q, w2sf, w2_alpha, keep=False, pool=None, x_gs=None):
     """Reference layer output.
 
     Shapes: x_bits (T, H) uint16 bf16 bits; topk_ids (T, k) int; topk_weights
     (T, k) float32; w13q (E, H/2, 2I) uint8; w13sf (E, H/16, 2I) uint8;
-    w13_alpha (E,) float32; w2q (E, I/2, H); w2sf (E, I/16, H); w2_alpha (E,).
+    w13_alpha (E,) float32, or (E, 2) for per-half weight global scales (gate,
+    up: column part p of w13[e] is scaled by gs1 * w13_alpha[e, p]);
+    w2q (E, I/2, H); w2sf (E, I/16, H); w2_alpha (E,).
+
+    x_gs: None for the dynamic activation scale gs1 = amax(x) / 2688, or a
+    float32 static scale used as gs1 (oracle.quantize.quantize_f32_static).
 
     Returns a dict with y (float64, unrounded), y_bits (bf16) and, when keep is
     set, the per-slot intermediates indexed [t, j]: gu (float64, unrounded),
@@ -102,7 +110,10 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     I = w2q.shape[1] * 2
 
     # stage 1
-    xq, xsf, gs1 = quantize_bf16(x_bits)
+    if x_gs is None:
+        xq, xsf, gs1 = quantize_bf16(x_bits)
+    else:
+        xq, xsf, gs1 = quantize_bf16_static(x_bits, x_gs)
 
     # stage 2
     groups = slots_by_expert(ids, E)
@@ -111,8 +122,9 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     # stage 3 + the SiLU half of stage 4
     act_bits = np.zeros((T, k, I), dtype=np.uint16)
     gu_keep = np.zeros((T, k, 2 * I), dtype=np.float64) if keep else None
+    w13a = np.asarray(w13_alpha, dtype=np.float32).astype(np.float64)
     tasks = [(xq[t_idx], xsf[t_idx], w13q[e], w13sf[e],
-              np.float64(gs1) * np.float64(np.float32(w13_alpha[e])), I, keep)
+              np.float64(gs1) * w13a[e], I, keep)
              for e, (t_idx, j_idx) in enumerate(groups) if t_idx.size]
     placed = [(t_idx, j_idx) for t_idx, j_idx in groups if t_idx.size]
     for (t_idx, j_idx), (act_e, gu_e) in zip(placed, _map(_l1_expert, tasks, pool)):

@@ -29,7 +29,11 @@ always gets scale byte 0x7E and its amax element magnitude 6.0 (closed form);
 the pages' own (amax, global scale) pairs 3.86 -> 1.4e-3 and 2.86e-4 -> 0.77
 (tests/golden/global_scale_pairs.txt); nibble order; sign symmetry Q(-x);
 power-of-two invariance Q(2^j x); the round-trip error bound; bit-for-bit
-agreement with the exact-rational twin in ``oracle.loops``.
+agreement with the exact-rational twin in ``oracle.loops``. The static-scale
+variant is pinned to the dynamic rule through its saturation property
+(Q_static(x, gs(c)) == Q(clamp(x, +-c)), tests/test_oracle_ext.py); the
+per-part weight rule is the per-matrix rule on each part, pinned through the
+layer invariants there (equal part scales reproduce the per-matrix layer).
 """
 import numpy as np
 
@@ -56,9 +60,25 @@ def quantize_f32(x):
     x = np.asarray(x, dtype=F32)
     if x.ndim != 2 or x.shape[1] % BLOCK:
         raise ValueError("quantize expects a 2-D array with cols % 16 == 0")
-    rows, cols = x.shape
     amax = F32(np.abs(x).max()) if x.size else F32(0.0)
-    gs = global_scale(amax)
+    return quantize_f32_static(x, global_scale(amax))
+
+
+def quantize_f32_static(x, gs):
+    """Steps 2-4 of the rule with a global scale given by the caller.
+
+    The static variant of stage_activation: gs is a fixed (e.g. calibrated)
+    activation scale instead of amax / 2688 of this tensor (the later DEBUG_LOG
+    revision discusses the checkpoint's calibrated ``input_scale`` in that
+    role). Nothing else changes: a block whose amax exceeds 6 * 448 * gs gets
+    the largest scale (s is clamped to 448, byte 0x7E) and its elements
+    saturate at magnitude 6. Returns (q, sf, gs) like quantize_f32.
+    """
+    x = np.asarray(x, dtype=F32)
+    if x.ndim != 2 or x.shape[1] % BLOCK:
+        raise ValueError("quantize expects a 2-D array with cols % 16 == 0")
+    gs = F32(gs)
+    rows, cols = x.shape
     q = np.empty((rows, cols // 2), dtype=np.uint8)
     sf = np.empty((rows, cols // BLOCK), dtype=np.uint8)
     step = max(1, (1 << 18) // max(cols, 1))
@@ -106,6 +126,35 @@ def quantize_weight_bf16(w_bits):
     """
     q_t, sf_t, gs = quantize_bf16(np.ascontiguousarray(np.asarray(w_bits).T))
     return np.ascontiguousarray(q_t.T), np.ascontiguousarray(sf_t.T), gs
+
+
+def quantize_bf16_static(x_bits, gs):
+    """quantize_f32_static on bf16 input bits."""
+    return quantize_f32_static(bf16_to_f32(x_bits), gs)
+
+
+def quantize_weight_bf16_parts(w_bits, parts):
+    """Weight rule with one global scale per column part.
+
+    W (K, N) is split along N into `parts` equal column ranges; each range is
+    quantized with the weight rule on its own (its own amax), and the results
+    are concatenated back along N. For w13 = [gate | up] with parts = 2 this is
+    the per-half weight global scale of the DEBUG_LOG ("Bugs Fixed", BF16
+    reference item 4: a global scale of shape (2,), applied per half) and of
+    the later revision's code-review item 5 (scaling the up half by the ratio
+    of the halves' scales is a per-column alpha).
+
+    Returns (q (K/2, N), sf (K/16, N), alphas float32 (parts,)).
+    """
+    w_bits = np.asarray(w_bits)
+    K, N = w_bits.shape
+    if parts < 1 or N % parts:
+        raise ValueError("N must be a multiple of parts")
+    w = N // parts
+    out = [quantize_weight_bf16(w_bits[:, p * w:(p + 1) * w]) for p in range(parts)]
+    q = np.concatenate([o[0] for o in out], axis=1)
+    sf = np.concatenate([o[1] for o in out], axis=1)
+    return q, sf, np.array([o[2] for o in out], dtype=F32)
 
 
 def unpack_nibbles(q, axis):
