@@ -117,6 +117,25 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * nvfp4_quantize_static - stage_activation with a global scale given by the
+ * caller instead of amax / 2688 of x (the later DEBUG_LOG revision, "input_scale
+ * red herring": a calibrated activation scale in that role; the pages found
+ * the checkpoint's calibrated value unsuitable for their runtime data, so the
+ * scale is entirely the caller's choice). Saves the amax pass.
+ *
+ *   x   (M, K) bf16, K % 16 == 0, 16-byte aligned
+ *   gs  one float32 (device), the global scale to use
+ *   q   (M, K/2) bytes out (8-byte aligned);  sf (M, K/16) bytes out
+ *
+ * The arithmetic is nvfp4_quantize's with gs taken as given: a block whose
+ * amax exceeds 6 * 448 * gs gets scale 448 (byte 0x7E) and its elements
+ * saturate at magnitude 6; gs <= 0 (or NaN) gives all-zero scale bytes and
+ * magnitudes (sign bits kept). M == 0 enqueues nothing. No workspace.
+ * ------------------------------------------------------------------------ */
+int nvfp4_quantize_static(const uint16_t* x, int64_t M, int64_t K, const float* gs,
+                          uint8_t* q, uint8_t* sf, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * nvfp4_quantize_weights - the loader's rule for a batch of E weight
  * matrices (DEBUG_LOG, Hypothesis 6 steps 1-5): per matrix one global scale,
  * blocks of 16 along K, output in the K-packed weight layout.
@@ -132,6 +151,27 @@ size_t nvfp4_quantize_weights_workspace(int64_t E, int64_t K, int64_t N);
 int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N,
                            uint8_t* q, uint8_t* sf, float* alpha,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_quantize_weights_parts - the weight rule with one global scale per
+ * column part: W[e] (K, N) is split along N into `parts` equal ranges and
+ * each range is quantized as its own matrix (own amax, own alpha). For w13 =
+ * [gate | up] with parts = 2 these are the per-half weight global scales of
+ * the DEBUG_LOG ("Bugs Fixed": a global scale of shape (2,) applied per half;
+ * later revision, code-review item 5: a per-column alpha), which the layer
+ * takes through nvfp4_moe_options.w13_alpha_per_half.
+ *
+ *   w, q, sf  as nvfp4_quantize_weights
+ *   alpha     (E, parts) float32 out: alpha[e][p] = amax(|W[e][:, part p]|) / 2688
+ *   1 <= parts <= 16, E * parts <= 65535, N % parts == 0, (N / parts) % 8 == 0,
+ *   else NVFP4_ESHAPE.
+ * Workspace: nvfp4_quantize_weights_parts_workspace(E, K, N, parts) bytes,
+ * 256-byte aligned. parts = 1 gives exactly nvfp4_quantize_weights' output.
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_quantize_weights_parts_workspace(int64_t E, int64_t K, int64_t N, int64_t parts);
+int nvfp4_quantize_weights_parts(const uint16_t* w, int64_t E, int64_t K, int64_t N,
+                                 int64_t parts, uint8_t* q, uint8_t* sf, float* alpha,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_operand_pitches - the padded row pitches of the packed weight layout
@@ -250,6 +290,57 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
                       int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
                       uint16_t* y, void* workspace, size_t workspace_bytes,
                       hipStream_t stream, hipEvent_t* stage_events);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_moe_forward_ex - nvfp4_moe_forward with options (a NULL options
+ * pointer, or a zero-initialized struct, is exactly nvfp4_moe_forward):
+ *
+ *   w13_alpha_per_half  0: w13_alpha is (E), one weight global scale per
+ *                       expert; 1: w13_alpha is (E, 2) float32, [e][0] for
+ *                       the gate columns [0, I) and [e][1] for the up columns
+ *                       [I, 2I) (nvfp4_quantize_weights_parts with parts = 2):
+ *                       stage 3 becomes gate = bf16((gs1 * w13_alpha[e][0]) *
+ *                       ...), up = bf16((gs1 * w13_alpha[e][1]) * ...).
+ *                       Other values: NVFP4_EINVAL.
+ *   x_global_scale      NULL: gs1 = amax(x) / 2688 (dynamic); else a device
+ *                       float32 (4-byte aligned) used as gs1 for stage 1, as
+ *                       in nvfp4_quantize_static (no amax pass; blocks beyond
+ *                       6 * 448 * gs1 saturate). gs2 stays dynamic.
+ * ------------------------------------------------------------------------ */
+typedef struct nvfp4_moe_options {
+    int32_t w13_alpha_per_half;
+    int32_t reserved;               /* 0 */
+    const float* x_global_scale;
+} nvfp4_moe_options;
+
+int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                         const uint8_t* w13, const uint8_t* w13_sf, const float* w13_alpha,
+                         const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha,
+                         int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                         uint16_t* y, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream, hipEvent_t* stage_events,
+                         const nvfp4_moe_options* options);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_route_topk - the router that produces the layer's topk_ids and
+ * topk_weights (the routing weights of the DEBUG_LOG's final "scatter with
+ * routing weights"; the pages do not define the router, this is the usual
+ * top-k with renormalized softmax):
+ *
+ *   logits        (T, E) float32, finite
+ *   topk_ids      (T, topk) int32 out: the topk largest logits of each row in
+ *                 descending order; among equal values the smaller expert
+ *                 index comes first
+ *   topk_weights  (T, topk) float32 out: exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *                 over the selected logits l_0 >= l_1 >= ..., float32, the sum
+ *                 in selection order (a renormalized softmax; rows sum to 1
+ *                 up to rounding)
+ *   1 <= topk <= E <= 512, T * E < 2^31, else NVFP4_ESHAPE; pointers 4-byte
+ *   aligned. T == 0 enqueues nothing. The ids are exact (comparisons of the
+ *   given float32 values); the weights carry float32 rounding and expf.
+ * ------------------------------------------------------------------------ */
+int nvfp4_route_topk(const float* logits, int64_t T, int64_t E, int64_t topk,
+                     int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
 #ifdef __cplusplus
 }

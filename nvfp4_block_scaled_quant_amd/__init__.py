@@ -5,13 +5,17 @@ kernels. PyTorch provides device memory and the current stream. The functions
 mirror the C ABI in include/nvfp4moe.h:
 
     quantize(x)                      -> (q, sf, gs)
+    quantize_static(x, gs)           -> (q, sf)           caller-given global scale
     quantize_weights(w)              -> (q, sf, alpha)    canonical weight layout
+    quantize_weights_parts(w, parts) -> (q, sf, alpha (E, parts))
     operand_pitches(K)               -> (ldq, ldsf, ldwsf)
     packed_shapes(E, K, N)           -> shapes of the packed weight tensors
     prepack_weights(q, sf)           -> (q_t, sf_t)       packed layout the GEMMs read
     gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
     moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
-                w2, w2_sf, w2_alpha, workspace=None, stage_events=None) -> y
+                w2, w2_sf, w2_alpha, workspace=None, stage_events=None,
+                x_gs=None) -> y          (w13_alpha (E,) or per half (E, 2))
+    route_topk(logits, topk)         -> (topk_ids, topk_weights)
 
 The library must be built in-tree first (``python -m
 nvfp4_block_scaled_quant_amd.build``); importing this package without it
@@ -46,7 +50,21 @@ _SIGS = {
     "nvfp4_moe_workspace": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_moe_workspace_layout": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
     "nvfp4_moe_forward": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _sz, _vp, _vp], _int),
+    "nvfp4_quantize_static": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "nvfp4_quantize_weights_parts_workspace": ([_i64, _i64, _i64, _i64], _sz),
+    "nvfp4_quantize_weights_parts": ([_vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
+                                     _int),
+    "nvfp4_moe_forward_ex": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _sz, _vp, _vp, _vp], _int),
+    "nvfp4_route_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
 }
+
+
+class MoeOptions(ctypes.Structure):
+    """struct nvfp4_moe_options."""
+    _fields_ = [("w13_alpha_per_half", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x_global_scale", ctypes.c_void_p)]
+
+
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
@@ -115,6 +133,55 @@ def quantize(x, q=None, sf=None, gs=None, workspace=None):
     _check(_lib.nvfp4_quantize(_ptr(x), M, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
                                ws.numel(), _stream()), "nvfp4_quantize")
     return q, sf, gs
+
+
+def quantize_static(x, gs, q=None, sf=None):
+    """NVFP4-quantize a bf16 (M, K) activation with the given global scale gs
+    (float32 (1,) on the device). Returns (q uint8 (M, K/2), sf uint8 (M, K/16))."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(gs, torch.float32, "gs", 1)
+    M, K = x.shape
+    dev = x.device
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
+    sf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    _check(_lib.nvfp4_quantize_static(_ptr(x), M, K, _ptr(gs), _ptr(q), _ptr(sf), _stream()),
+           "nvfp4_quantize_static")
+    return q, sf
+
+
+def quantize_weights_parts(w, parts):
+    """quantize_weights with one global scale per column part: W[e] (K, N)
+    split along N into `parts` equal ranges. Returns (q (E, K/2, N), sf
+    (E, K/16, N), alpha float32 (E, parts))."""
+    _need(w, torch.bfloat16, "w", 3)
+    E, K, N = w.shape
+    dev = w.device
+    q = torch.empty((E, K // 2, N), dtype=torch.uint8, device=dev)
+    sf = torch.empty((E, K // 16, N), dtype=torch.uint8, device=dev)
+    alpha = torch.empty((E, parts), dtype=torch.float32, device=dev)
+    nws = _lib.nvfp4_quantize_weights_parts_workspace(E, K, N, parts)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    _check(_lib.nvfp4_quantize_weights_parts(_ptr(w), E, K, N, parts, _ptr(q), _ptr(sf),
+                                             _ptr(alpha), _ptr(ws), ws.numel(), _stream()),
+           "nvfp4_quantize_weights_parts")
+    return q, sf, alpha
+
+
+def route_topk(logits, topk, ids=None, weights=None):
+    """Top-k router: logits float32 (T, E) -> (topk_ids int32 (T, topk),
+    topk_weights float32 (T, topk)), softmax renormalized over the selected."""
+    _need(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev) if ids is None else ids
+    weights = torch.empty((T, topk), dtype=torch.float32, device=dev) if weights is None else weights
+    _need(ids, torch.int32, "ids", 2)
+    _need(weights, torch.float32, "weights", 2)
+    if ids.shape != (T, topk) or weights.shape != (T, topk):
+        raise ValueError("route_topk: output shapes must be (T, topk)")
+    _check(_lib.nvfp4_route_topk(_ptr(logits), T, E, topk, _ptr(ids), _ptr(weights), _stream()),
+           "nvfp4_route_topk")
+    return ids, weights
 
 
 def quantize_weights(w):
@@ -208,10 +275,12 @@ def moe_workspace_layout(T, H, I, E, topk):
 
 
 def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
-                y=None, workspace=None, stage_events=None):
+                y=None, workspace=None, stage_events=None, x_gs=None):
     """The five-stage NVFP4 expert layer. Weights in the packed layout
     (prepack_weights of the canonical (E, H/2, 2I) and (E, I/2, H) tensors).
 
+    w13_alpha: (E,) one weight global scale per expert, or (E, 2) per half
+    (gate, up). x_gs: None (dynamic gs1) or a float32 (1,) static gs1.
     stage_events: None or a StageEvents; returns y (T, H) bf16.
     """
     _need(x, torch.bfloat16, "x", 2)
@@ -219,8 +288,10 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     _need(topk_weights, torch.float32, "topk_weights", 2)
     for t, n in ((w13, "w13"), (w13_sf, "w13_sf"), (w2, "w2"), (w2_sf, "w2_sf")):
         _need(t, torch.uint8, n, 5)
-    _need(w13_alpha, torch.float32, "w13_alpha", 1)
+    _need(w13_alpha, torch.float32, "w13_alpha")
     _need(w2_alpha, torch.float32, "w2_alpha", 1)
+    if x_gs is not None:
+        _need(x_gs, torch.float32, "x_gs", 1)
     T, H = x.shape
     topk = topk_ids.shape[1]
     E = w13.shape[0]
@@ -231,7 +302,7 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     s2, s2f = packed_shapes(E, I, H)
     if (tuple(w13.shape) != s13 or tuple(w13_sf.shape) != s13f
             or tuple(w2.shape) != s2 or tuple(w2_sf.shape) != s2f
-            or w13_alpha.shape != (E,) or w2_alpha.shape != (E,)
+            or w13_alpha.shape not in ((E,), (E, 2)) or w2_alpha.shape != (E,)
             or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
         raise ValueError("moe_forward: inconsistent shapes")
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if y is None else y
@@ -239,10 +310,19 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     if workspace is None:
         workspace = torch.empty((nws,), dtype=torch.uint8, device=x.device)
     ev = stage_events.handles if stage_events is not None else None
-    _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
-                                  _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
-                                  _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
-                                  workspace.numel(), _stream(), ev), "nvfp4_moe_forward")
+    per_half = w13_alpha.dim() == 2
+    if not per_half and x_gs is None:
+        _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
+                                      _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
+                                      _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
+                                      workspace.numel(), _stream(), ev), "nvfp4_moe_forward")
+        return y
+    opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None)
+    _check(_lib.nvfp4_moe_forward_ex(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
+                                     _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
+                                     _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
+                                     workspace.numel(), _stream(), ev, ctypes.byref(opts)),
+           "nvfp4_moe_forward_ex")
     return y
 
 

@@ -108,7 +108,7 @@ const char* nvfp4_strerror(int status) {
     }
 }
 
-int nvfp4_version(void) { return (3 << 16) | 0; }
+int nvfp4_version(void) { return (3 << 16) | 1; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -135,11 +135,30 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t*
     return NVFP4_OK;
 }
 
+int nvfp4_quantize_static(const uint16_t* x, int64_t M, int64_t K, const float* gs, uint8_t* q,
+                          uint8_t* sf, hipStream_t stream) {
+    if (M < 0 || K <= 0) return NVFP4_EINVAL;
+    if (K % 16) return NVFP4_ESHAPE;
+    if (M == 0) return NVFP4_OK;
+    if (!x || !gs || !q || !sf) return NVFP4_EINVAL;
+    if (!aligned(x, 16) || !aligned(q, 8) || !aligned(gs, 4)) return NVFP4_EINVAL;
+    int dv = check_device();
+    if (dv) return dv;
+    NVFP4_TRY(launch_quant_rows(x, M, K, nullptr, nullptr, q, K / 2, sf, K / 16, nullptr, stream, gs));
+    return NVFP4_OK;
+}
+
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_weights_workspace(int64_t E, int64_t K, int64_t N) {
     (void)K;
     (void)N;
     return align_up((size_t)(E > 0 ? E : 1) * 4);
+}
+
+size_t nvfp4_quantize_weights_parts_workspace(int64_t E, int64_t K, int64_t N, int64_t parts) {
+    (void)K;
+    (void)N;
+    return align_up((size_t)(E > 0 ? E : 1) * (size_t)(parts > 0 ? parts : 1) * 4);
 }
 
 int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N, uint8_t* q,
@@ -158,7 +177,27 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N, u
     uint32_t* slots = static_cast<uint32_t*>(workspace);
     NVFP4_TRY(launch_zero_u32(slots, (int)E, stream));
     NVFP4_TRY(launch_amax_bf16_batched(w, E, K * N, slots, stream));
-    NVFP4_TRY(launch_quant_cols(w, E, K, N, slots, q, sf, alpha, stream));
+    NVFP4_TRY(launch_quant_cols(w, E, K, N, 1, slots, q, sf, alpha, stream));
+    return NVFP4_OK;
+}
+
+int nvfp4_quantize_weights_parts(const uint16_t* w, int64_t E, int64_t K, int64_t N, int64_t parts,
+                                 uint8_t* q, uint8_t* sf, float* alpha, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    if (E < 0 || K <= 0 || N <= 0 || parts <= 0) return NVFP4_EINVAL;
+    if (K % 16 || E * parts > 65535 || parts > 16 || N % parts || (N / parts) % 8) return NVFP4_ESHAPE;
+    if (E == 0) return NVFP4_OK;
+    if (!w || !q || !sf || !alpha) return NVFP4_EINVAL;
+    if (!aligned(w, 16) || !aligned(alpha, 4)) return NVFP4_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign) ||
+        workspace_bytes < nvfp4_quantize_weights_parts_workspace(E, K, N, parts))
+        return NVFP4_EWORKSPACE;
+    int dv = check_device();
+    if (dv) return dv;
+    uint32_t* slots = static_cast<uint32_t*>(workspace);
+    NVFP4_TRY(launch_zero_u32(slots, (int)(E * parts), stream));
+    NVFP4_TRY(launch_amax_cols(w, E, K, N, (int)parts, slots, stream));
+    NVFP4_TRY(launch_quant_cols(w, E, K, N, (int)parts, slots, q, sf, alpha, stream));
     return NVFP4_OK;
 }
 
@@ -237,7 +276,22 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
                       const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha, int64_t T,
                       int64_t H, int64_t I, int64_t E, int64_t topk, uint16_t* y, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+    return nvfp4_moe_forward_ex(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf,
+                                w2_alpha, T, H, I, E, topk, y, workspace, workspace_bytes, stream,
+                                stage_events, nullptr);
+}
+
+int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                         const uint8_t* w13, const uint8_t* w13_sf, const float* w13_alpha,
+                         const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha, int64_t T,
+                         int64_t H, int64_t I, int64_t E, int64_t topk, uint16_t* y, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events,
+                         const nvfp4_moe_options* options) {
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return NVFP4_EINVAL;
+    const int per_half = options ? options->w13_alpha_per_half : 0;
+    const float* x_gs = options ? options->x_global_scale : nullptr;
+    if (per_half != 0 && per_half != 1) return NVFP4_EINVAL;
+    if (x_gs && !aligned(x_gs, 4)) return NVFP4_EINVAL;
     if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
     if (!w13 || !w13_sf || !w13_alpha || !w2 || !w2_sf || !w2_alpha) return NVFP4_EINVAL;
     if (T > 0 && (!x || !topk_ids || !topk_weights || !y)) return NVFP4_EINVAL;
@@ -287,15 +341,16 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     // A small x is quantized by a second work-group of the routing launch
     // (stage 2 is then empty); a larger one by the amax and block kernels.
     const bool small_x = T * H <= kSmallQuantMax;
-    const SmallQuant sq = {x, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
+    const SmallQuant sq = {x, x_gs, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
     NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
                            slot_row, tiles, num_tiles, amax, 2, small_x ? &sq : nullptr, stream));
     // 2. quantize x
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
     if (!small_x) {
-        NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
+        // a static global scale (x_gs) needs no amax pass
+        if (!x_gs) NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
         NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, pitch_q(H), xsf, pitch_sf(H), gs1,
-                                    stream));
+                                    stream, x_gs));
     }
     // 3. L1 grouped GEMM with fused SiLU(gate) * up
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
@@ -312,6 +367,7 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     p1.K = H;
     p1.a_gs = gs1;
     p1.b_alpha = w13_alpha;
+    p1.alpha_stride = per_half ? 2 : 1;
     p1.tiles = tiles;
     p1.num_tiles = num_tiles;
     p1.max_tiles = max_tiles;
@@ -346,6 +402,19 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
     NVFP4_TRY(launch_combine(o2, slot_row, topk_weights, T, (int)topk, H, y, stream));
     NVFP4_TRY(mark(NVFP4_MOE_NUM_STAGES));
     return NVFP4_OK;
+}
+
+// ---------------------------------------------------------------------------
+int nvfp4_route_topk(const float* logits, int64_t T, int64_t E, int64_t topk, int32_t* topk_ids,
+                     float* topk_weights, hipStream_t stream) {
+    if (T < 0 || E <= 0 || topk <= 0) return NVFP4_EINVAL;
+    if (topk > E || E > kMaxExperts || T >= ((int64_t)1 << 31) / E) return NVFP4_ESHAPE;
+    if (T == 0) return NVFP4_OK;
+    if (!logits || !topk_ids || !topk_weights) return NVFP4_EINVAL;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4)) return NVFP4_EINVAL;
+    int dv = check_device();
+    if (dv) return dv;
+    return hip_status(launch_route_topk(logits, T, (int)E, (int)topk, topk_ids, topk_weights, stream));
 }
 
 }  // extern "C"

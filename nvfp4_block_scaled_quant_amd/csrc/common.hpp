@@ -116,6 +116,16 @@ __device__ __forceinline__ QuantScales make_scales(float amax) {
     return s;
 }
 
+// A global scale given by the caller (static activation scale): the rest of
+// the rule is unchanged, so blocks beyond 6 * 448 * gs saturate (scale 448,
+// magnitude 6).
+__device__ __forceinline__ QuantScales scales_from_gs(float gs) {
+    QuantScales s;
+    s.gs = gs;
+    s.six_gs = 6.0f * gs;
+    return s;
+}
+
 // E4M3FN code nearest to s in [0, 448], ties to the even code.
 // Subnormal range (s < 2^-6): spacing 2^-9, code = rint(s * 2^9).
 // Normal range: with e = floor(log2 s) in [-6, 8], r = rint(s * 2^(3-e)) in

@@ -309,8 +309,11 @@ void gemm_kernel(GemmParams p) {
 
     // ---- epilogue ------------------------------------------------------------
     // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
-    const float alpha = p.a_gs[0] * p.b_alpha[expert];
+    // L1 with per-half weight scales: gate columns take alpha, up alpha_up
+    const int ast = (MODE == kGemmL1 && p.alpha_stride > 1) ? 2 : 1;
+    const float alpha = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast];
     if (MODE == kGemmL1) {
+        const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
         // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
         // The rounded (gate, up) pairs of one half of the tile (128 rows x 128
         // act columns) go through the now idle LDS; then all threads apply
@@ -328,7 +331,7 @@ void gemm_kernel(GemmParams p) {
                             const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                             const int col = wn * 64 + 32 * j + l32;
                             const uint32_t g = f32_to_bf16_rne(alpha * acc[i][j][r]);
-                            const uint32_t u = f32_to_bf16_rne(alpha * acc[i][j + 2][r]);
+                            const uint32_t u = f32_to_bf16_rne(alpha_up * acc[i][j + 2][r]);
                             gu[row * 128 + col] = g | (u << 16);
                         }
             }

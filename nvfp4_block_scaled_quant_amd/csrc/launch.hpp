@@ -32,12 +32,14 @@ hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* slot, hipStr
 hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, uint32_t* slots,
                                     hipStream_t s);
 
-// Row-block quantization of x (M, K) with amax taken from *amax_slot. Rows at or
-// beyond *m_dev (when m_dev is not null) are left untouched. gs_out receives gs.
+// Row-block quantization of x (M, K) with amax taken from *amax_slot, or with
+// the global scale *gs_in when gs_in is not null. Rows at or beyond *m_dev
+// (when m_dev is not null) are left untouched. gs_out receives gs.
 // Output rows are ldq bytes (q) and ldsf bytes (sf) apart.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
                              const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
-                             int64_t ldsf, float* gs_out, hipStream_t s);
+                             int64_t ldsf, float* gs_out, hipStream_t s,
+                             const float* gs_in = nullptr);
 
 // Row pitches of the GEMM operand layout: packed data padded to whole
 // 128-element K steps, scales to whole 8-byte steps.
@@ -70,8 +72,14 @@ __host__ __device__ inline int64_t wsf_off(int64_t n, int64_t ldsf, int64_t st, 
 hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t C, uint8_t* out,
                                int64_t ldo, bool scale_layout, hipStream_t s);
 
-// Column-block quantization of E weight matrices (E, K, N) with per-matrix amax.
-hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
+// Per-part amax of E weight matrices (E, K, N), each split along N into
+// `parts` equal column ranges (N / parts % 8 == 0), into slots[e * parts + p].
+hipError_t launch_amax_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N, int parts,
+                            uint32_t* slots, hipStream_t s);
+
+// Column-block quantization of E weight matrices (E, K, N), one amax (and one
+// alpha out) per column part: amax_slots / alpha [e * parts + p].
+hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N, int parts,
                              const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
                              hipStream_t s);
 
@@ -79,6 +87,7 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
 // work-groups (each reduces the whole amax, then quantizes its share).
 struct SmallQuant {
     const uint16_t* x;
+    const float* gs_in;      // static global scale, or null for amax / 2688
     int64_t M, K;
     uint8_t* q;
     int64_t ldq;
@@ -95,6 +104,12 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, 
                         int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
                         int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
                         hipStream_t s);
+
+// Top-k router: ids (T, k) = the k largest logits of each row of (T, E)
+// (ties: smaller expert first), weights (T, k) = softmax over the selected
+// logits. E <= kMaxExperts, 1 <= k <= E.
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                             float* weights, hipStream_t s);
 
 // y[t] = bf16(sum_j w[t][j] * o2[slot_row[t*topk+j]]) for rows that exist.
 hipError_t launch_combine(const float* o2, const int32_t* slot_row, const float* weights,
@@ -118,7 +133,8 @@ struct GemmParams {
     int64_t N;                 // columns of B
     int64_t K;
     const float* a_gs;         // device scalar
-    const float* b_alpha;      // device, one per expert
+    const float* b_alpha;      // device, alpha_stride per expert
+    int alpha_stride;          // L1: 2 = (gate, up) per expert, else 1
     // grouped tiles
     const Tile* tiles;
     const int32_t* num_tiles;

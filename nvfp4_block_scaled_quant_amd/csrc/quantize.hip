@@ -64,14 +64,16 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
     block_atomic_max(m, slots + blockIdx.y);
 }
 
-// One thread per 16-element block of a row-major (M, K) bf16 matrix.
+// One thread per 16-element block of a row-major (M, K) bf16 matrix. The
+// global scale is amax / 2688 of *amax_slot, or *gs_in when gs_in is not null
+// (static scale); either way it is also written to *gs_out when gs_out is not
+// null.
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ m_dev,
-    const uint32_t* __restrict__ amax_slot, uint8_t* __restrict__ q, int64_t ldq,
-    uint8_t* __restrict__ sf, int64_t ldsf, float* __restrict__ gs_out) {
-    const float amax = __uint_as_float(*amax_slot);
-    const QuantScales qs = make_scales(amax);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *gs_out = qs.gs;
+    const uint32_t* __restrict__ amax_slot, const float* __restrict__ gs_in, uint8_t* __restrict__ q,
+    int64_t ldq, uint8_t* __restrict__ sf, int64_t ldsf, float* __restrict__ gs_out) {
+    const QuantScales qs = gs_in ? scales_from_gs(*gs_in) : make_scales(__uint_as_float(*amax_slot));
+    if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = qs.gs;
     const int64_t rows = m_dev ? min((int64_t)(*m_dev), M) : M;
     const int64_t groups = K / 16;
     const int64_t nblocks = rows * groups;
@@ -108,21 +110,44 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
     }
 }
 
+// Per-part amax of E row-major (K, N) matrices split along N into `parts`
+// column ranges of width Np (Np % 8 == 0): slot e * parts + p.
+__global__ __launch_bounds__(kThreads) void amax_cols_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                             int64_t N, int64_t Np, int parts,
+                                                             uint32_t* __restrict__ slots) {
+    const int64_t e = blockIdx.y / parts, part = blockIdx.y - e * parts;
+    const uint16_t* base = x + e * K * N + part * Np;
+    const int64_t vrow = Np / 8, nvec = K * vrow;
+    uint32_t m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = i / vrow, c = i - r * vrow;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + r * N + 8 * c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) m = max(m, max(v[k] & 0x7FFFu, (v[k] >> 16) & 0x7FFFu));
+    }
+    block_atomic_max(m, slots + blockIdx.y);
+}
+
 // One thread per (matrix e, K-group g, column n) of E row-major (K, N) bf16
 // matrices; blocks run along K. Output byte [e][8g + j][n] holds the nibbles
-// of k = 16g + 2j (low) and 16g + 2j + 1 (high).
+// of k = 16g + 2j (low) and 16g + 2j + 1 (high). Column n belongs to part
+// n / Np of its matrix, whose amax is amax_slots[e * parts + n / Np] and whose
+// global scale goes to alpha[e * parts + n / Np].
 __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
-    const uint16_t* __restrict__ w, int64_t K, int64_t N, const uint32_t* __restrict__ amax_slots,
-    uint8_t* __restrict__ q, uint8_t* __restrict__ sf, float* __restrict__ alpha) {
+    const uint16_t* __restrict__ w, int64_t K, int64_t N, int64_t Np, int parts,
+    const uint32_t* __restrict__ amax_slots, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+    float* __restrict__ alpha) {
     const int64_t e = blockIdx.y;
-    const QuantScales qs = make_scales(__uint_as_float(amax_slots[e]));
     const int64_t groups = K / 16;
     const int64_t per = groups * N;
     const uint16_t* we = w + e * K * N;
-    if (blockIdx.x == 0 && threadIdx.x == 0) alpha[e] = qs.gs;
+    if (blockIdx.x == 0 && threadIdx.x < parts)
+        alpha[e * parts + threadIdx.x] = make_scales(__uint_as_float(amax_slots[e * parts + threadIdx.x])).gs;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < per;
          i += (int64_t)gridDim.x * kThreads) {
         const int64_t g = i / N, n = i - g * N;
+        const QuantScales qs = make_scales(__uint_as_float(amax_slots[e * parts + n / Np]));
         uint32_t v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -173,9 +198,9 @@ hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, u
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
                              const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
-                             int64_t ldsf, float* gs_out, hipStream_t s) {
+                             int64_t ldsf, float* gs_out, hipStream_t s, const float* gs_in) {
     const int g = grid_for(M * (K / 16), 1 << 20);
-    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, q, ldq, sf, ldsf, gs_out);
+    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, gs_in, q, ldq, sf, ldsf, gs_out);
     return hipGetLastError();
 }
 
@@ -189,12 +214,22 @@ hipError_t launch_pack_weights(const uint8_t* in, int64_t E, int64_t R, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
+hipError_t launch_amax_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N, int parts,
+                            uint32_t* slots, hipStream_t s) {
+    if (E <= 0 || parts <= 0) return hipSuccess;
+    const int64_t Np = N / parts;
+    const int g = grid_for(K * Np / 8, 512);
+    amax_cols_kernel<<<dim3(g, (unsigned)(E * parts)), kThreads, 0, s>>>(w, K, N, Np, parts, slots);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N, int parts,
                              const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
                              hipStream_t s) {
     if (E <= 0) return hipSuccess;
     const int g = grid_for((K / 16) * N, 4096);
-    quant_cols_kernel<<<dim3(g, (unsigned)E), kThreads, 0, s>>>(w, K, N, amax_slots, q, sf, alpha);
+    quant_cols_kernel<<<dim3(g, (unsigned)E), kThreads, 0, s>>>(w, K, N, N / parts, parts, amax_slots,
+                                                                  q, sf, alpha);
     return hipGetLastError();
 }
 

@@ -36,22 +36,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         // small activation: every quantization work-group reduces the amax of
         // all of x (a few hundred KB at most, from L2) and then quantizes its
         // own share of the 16-element blocks
+        // (with a static global scale the amax is not needed)
         __shared__ uint32_t wmax[kWaves];
         const int tid = threadIdx.x;
-        const int64_t n = xq.M * xq.K;
-        const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
-        uint32_t m = 0;
-        for (int64_t i = tid; i < n / 8; i += kRouteThreads) {
-            const u32x4 w = v[i];
+        QuantScales qs;
+        if (xq.gs_in) {
+            qs = scales_from_gs(*xq.gs_in);
+        } else {
+            const int64_t n = xq.M * xq.K;
+            const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
+            uint32_t m = 0;
+            for (int64_t i = tid; i < n / 8; i += kRouteThreads) {
+                const u32x4 w = v[i];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7FFFu, (w[c] >> 16) & 0x7FFFu));
+                for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7FFFu, (w[c] >> 16) & 0x7FFFu));
+            }
+            m = wave_max_u32(m);
+            if ((tid & 63) == 0) wmax[tid >> 6] = m;
+            __syncthreads();
+            m = wmax[0];
+            for (int w = 1; w < kWaves; ++w) m = max(m, wmax[w]);
+            qs = make_scales(__uint_as_float(m << 16));
         }
-        m = wave_max_u32(m);
-        if ((tid & 63) == 0) wmax[tid >> 6] = m;
-        __syncthreads();
-        m = wmax[0];
-        for (int w = 1; w < kWaves; ++w) m = max(m, wmax[w]);
-        const QuantScales qs = make_scales(__uint_as_float(m << 16));
         if (blockIdx.x == 1 && tid == 0) *xq.gs = qs.gs;
         const int64_t groups = xq.K / 16;
         for (int64_t b = (int64_t)(blockIdx.x - 1) * kRouteThreads + tid; b < xq.M * groups;
@@ -242,6 +248,80 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     *reinterpret_cast<u32x4*>(y + t * H + c0) = out;
 }
 
+// Top-k router with renormalized softmax weights, one wave per token: each
+// lane holds the logits of experts lane, lane + 64, ... (up to 512 experts);
+// k rounds of a wave-wide arg-max over the experts not yet taken, the larger
+// value winning and the smaller expert index among equal values; then
+// w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected logits, l_0
+// the largest, the sum taken in selection order. float32 throughout.
+constexpr int kTopkWaves = 4;
+constexpr int kTopkPerLane = kMaxExperts / 64;
+
+__global__ __launch_bounds__(64 * kTopkWaves) void route_topk_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
+    if (t >= T) return;                       // uniform per wave
+    const float* row = logits + t * E;
+    float v[kTopkPerLane];
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i) {
+        const int e = 64 * i + lane;
+        v[i] = e < E ? row[e] : 0.0f;
+    }
+    uint32_t avail = 0;                       // bit i: expert 64 i + lane is a candidate
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i)
+        if (64 * i + lane < E) avail |= 1u << i;
+    int32_t sel_id[kTopkPerLane];
+    float sel_e[kTopkPerLane];
+    float top = 0.0f, sum = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        // this lane's best candidate (entries are in ascending expert order,
+        // so a strict comparison keeps the smallest index among equal values)
+        float bv = 0.0f;
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < kTopkPerLane; ++i)
+            if (((avail >> i) & 1u) && (bi == 0x7FFFFFFF || v[i] > bv)) {
+                bv = v[i];
+                bi = 64 * i + lane;
+            }
+        // wave arg-max: larger value, then smaller index; lanes without a
+        // candidate carry index INT_MAX and lose to every real one
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            const bool other = (oi != 0x7FFFFFFF) &&
+                               (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+            if (other) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+        if (j == 0) top = bv;
+        const float ej = expf(bv - top);
+        sum += ej;
+#pragma unroll
+        for (int i = 0; i < kTopkPerLane; ++i)
+            if (j == 64 * i + lane) {
+                sel_id[i] = bi;
+                sel_e[i] = ej;
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < kTopkPerLane; ++i) {
+        const int j = 64 * i + lane;
+        if (j < k) {
+            ids[t * k + j] = sel_id[i];
+            weights[t * k + j] = sel_e[i] / sum;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
@@ -266,6 +346,18 @@ hipError_t launch_combine(const float* o2, const int32_t* slot_row, const float*
     if (T <= 0) return hipSuccess;
     const int chunks = (int)((H / 8 + 255) / 256);
     combine_kernel<<<(unsigned)(T * chunks), 256, 0, s>>>(o2, slot_row, weights, topk, H, chunks, y);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                             float* weights, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    const int64_t grid = (T + kTopkWaves - 1) / kTopkWaves;
+    route_topk_kernel<<<(unsigned)grid, 64 * kTopkWaves, 0, s>>>(logits, T, E, k, ids, weights);
     return hipGetLastError();
 }
 

@@ -277,8 +277,11 @@ void skinny_kernel(GemmParams p) {
     }
 
     // ---- epilogue: acc[f][i] = D[tile row 4q + i][column c of block f] --------
-    const float alpha = p.a_gs[0] * p.b_alpha[expert];
+    // L1 with per-half weight scales: gate columns take alpha, up alpha_up
+    const int ast = (MODE == kGemmL1 && p.alpha_stride > 1) ? 2 : 1;
+    const float alpha = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast];
     if (MODE == kGemmL1) {
+        const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
         uint32_t amax_bits = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -289,7 +292,7 @@ void skinny_kernel(GemmParams p) {
             for (int f = 0; f < GB; ++f) {
                 if (!ok[f]) continue;
                 const float g = bf16_to_f32(f32_to_bf16_rne(alpha * acc[f][i]));
-                const float u = bf16_to_f32(f32_to_bf16_rne(alpha * acc[f + GB][i]));
+                const float u = bf16_to_f32(f32_to_bf16_rne(alpha_up * acc[f + GB][i]));
                 const uint32_t a = silu_mul_bf16(g, u);
                 amax_bits = max(amax_bits, a & 0x7FFFu);
                 p.out_bf16[prow * p.I + col0 + 16 * f + c] = (uint16_t)a;

@@ -99,12 +99,15 @@ def bf16_ulp_distance(a_bits, b_bits):
     return np.abs(key(a_bits) - key(b_bits))
 
 
-def make_layer(cfg, experts=None):
+def make_layer(cfg, experts=None, w13_parts=1, up_scale=1.0):
     """Oracle-side inputs of a layer config: x, routing, weights quantized with
     the oracle's rule (O-Q along K). `experts` limits which experts get real
-    weights (the others are zero and must be unused by the routing)."""
+    weights (the others are zero and must be unused by the routing).
+    w13_parts = 2 quantizes gate and up with their own global scales (w13a
+    becomes (E, 2)); up_scale multiplies the up half of the bf16 weights first
+    (a power of two keeps them exact)."""
     import workloads as W
-    from oracle.quantize import quantize_weight_bf16
+    from oracle.quantize import quantize_weight_bf16, quantize_weight_bf16_parts
     x = W.activations(cfg)
     ids, wts = W.routing(cfg)
     E, H, I = cfg.E, cfg.H, cfg.I
@@ -112,11 +115,19 @@ def make_layer(cfg, experts=None):
     w13sf = np.zeros((E, H // 16, 2 * I), np.uint8)
     w2q = np.zeros((E, I // 2, H), np.uint8)
     w2sf = np.zeros((E, I // 16, H), np.uint8)
-    w13a = np.zeros(E, np.float32)
+    w13a = np.zeros(E, np.float32) if w13_parts == 1 else np.zeros((E, w13_parts), np.float32)
     w2a = np.zeros(E, np.float32)
     for e in (range(E) if experts is None else experts):
         w13, w2 = W.expert_weights_bf16(cfg, e)
-        w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16(w13)
+        if up_scale != 1.0:
+            from oracle.formats import bf16_from_f64, bf16_to_f32
+            f = bf16_to_f32(w13).astype(np.float64)
+            f[:, I:] *= up_scale
+            w13 = bf16_from_f64(f)
+        if w13_parts == 1:
+            w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16(w13)
+        else:
+            w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16_parts(w13, w13_parts)
         w2q[e], w2sf[e], w2a[e] = quantize_weight_bf16(w2)
     if cfg.alpha_loguniform:
         w13a, w2a = W.alphas_loguniform(cfg)
@@ -127,7 +138,8 @@ def make_layer(cfg, experts=None):
 def run_oracle_layer(L, keep=True, pool=None):
     from oracle.moe import moe_forward
     return moe_forward(L["x"], L["ids"], L["wts"], L["w13q"], L["w13sf"], L["w13a"],
-                       L["w2q"], L["w2sf"], L["w2a"], keep=keep, pool=pool)
+                       L["w2q"], L["w2sf"], L["w2a"], keep=keep, pool=pool,
+                       x_gs=L.get("x_gs"))
 
 
 def gpu_packed_weights(nv, L):
@@ -152,10 +164,11 @@ def run_gpu_layer(nv, L, repeat=1, packed=None):
     I = L["w2q"].shape[1] * 2
     nws = nv.moe_workspace_size(T, H, I, E, k)
     ws = torch.empty((nws,), dtype=torch.uint8, device="cuda")
+    x_gs = to_dev(np.array([L["x_gs"]], np.float32)) if L.get("x_gs") is not None else None
     ys = []
     for _ in range(repeat):
         y = nv.moe_forward(d["x"], d["ids"], d["wts"], pw["w13"], pw["w13_sf"], pw["w13a"],
-                           pw["w2"], pw["w2_sf"], pw["w2a"], workspace=ws)
+                           pw["w2"], pw["w2_sf"], pw["w2a"], workspace=ws, x_gs=x_gs)
         ys.append(to_host(y))
     torch.cuda.synchronize()
     lay = nv.moe_workspace_layout(T, H, I, E, k)

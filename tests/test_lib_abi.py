@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("nvfp4_quantize", "nvfp4_moe_forward", "nvfp4_gemm", "nvfp4_strerror",
                  "nvfp4_quantize_weights", "nvfp4_moe_workspace", "nvfp4_prepack_weights",
-                 "nvfp4_operand_pitches"):
+                 "nvfp4_operand_pitches", "nvfp4_quantize_static", "nvfp4_quantize_weights_parts",
+                 "nvfp4_moe_forward_ex", "nvfp4_route_topk"):
         assert must in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (3, 0)
+    assert nv.version() == (3, 1)
     for code in range(6):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
@@ -140,6 +141,55 @@ def test_moe_argument_errors(nv):
     assert call(8, 7168, 3072, 48, 8, ptrs=[p(A16 + 4)] + ptrs9[1:]) == 1   # x misaligned
     assert call(8, 7168, 3072, 48, 8, ptrs=ptrs9[:3] + [p(0)] + ptrs9[4:]) == 1
     assert call(8, 7168, 3072, 48, 8, y=0) == 1
+
+
+def test_moe_forward_ex_option_errors(nv):
+    f = lib(nv).nvfp4_moe_forward_ex
+    ptrs9 = [p(A16)] * 9
+
+    def call(opts, T=8):
+        ref = ctypes.byref(opts) if opts is not None else None
+        return f(*ptrs9, T, 7168, 3072, 48, 8, p(A16), p(A16), 1024, None, None, ref)
+
+    # a null options pointer is nvfp4_moe_forward: same validation order
+    assert call(None) == 3                                   # workspace too small
+    assert call(nv.MoeOptions(2, 0, None)) == 1              # per_half must be 0 or 1
+    assert call(nv.MoeOptions(-1, 0, None)) == 1
+    assert call(nv.MoeOptions(0, 0, A16 + 2)) == 1           # misaligned static scale
+    assert call(nv.MoeOptions(1, 0, A16)) == 3               # valid options, then the workspace
+    assert call(nv.MoeOptions(1, 0, A16), T=0) == 3
+
+
+def test_quantize_static_argument_errors(nv):
+    f = lib(nv).nvfp4_quantize_static
+    assert f(p(A16), 4, 40, p(A16), p(A16), p(A16), None) == 2      # K % 16
+    assert f(p(A16), -1, 32, p(A16), p(A16), p(A16), None) == 1
+    assert f(p(A16), 4, 32, p(0), p(A16), p(A16), None) == 1        # gs null
+    assert f(p(A16 + 2), 4, 32, p(A16), p(A16), p(A16), None) == 1  # x alignment
+    assert f(p(0), 0, 32, p(0), p(0), p(0), None) == 0              # M == 0: nothing
+
+
+def test_quantize_weights_parts_argument_errors(nv):
+    f = lib(nv).nvfp4_quantize_weights_parts
+    ws = lib(nv).nvfp4_quantize_weights_parts_workspace
+    assert ws(48, 7168, 6144, 2) >= 48 * 2 * 4
+    assert f(p(A16), 2, 64, 48, 5, p(A16), p(A16), p(A16), p(A16), 1 << 20, None) == 2   # N % parts
+    assert f(p(A16), 2, 64, 60, 5, p(A16), p(A16), p(A16), p(A16), 1 << 20, None) == 2   # N/parts % 8
+    assert f(p(A16), 2, 64, 48, 0, p(A16), p(A16), p(A16), p(A16), 1 << 20, None) == 1
+    assert f(p(A16), 2, 64, 48, 17, p(A16), p(A16), p(A16), p(A16), 1 << 20, None) == 2
+    assert f(p(A16), 2, 64, 48, 2, p(A16), p(A16), p(A16), p(A16), 8, None) == 3         # workspace
+    assert f(p(A16), 0, 64, 48, 2, p(0), p(0), p(0), p(0), 0, None) == 0                 # E == 0
+
+
+def test_route_topk_argument_errors(nv):
+    f = lib(nv).nvfp4_route_topk
+    assert f(p(A16), 16, 48, 49, p(A16), p(A16), None) == 2         # topk > E
+    assert f(p(A16), 16, 513, 8, p(A16), p(A16), None) == 2         # E above the maximum
+    assert f(p(A16), 16, 48, 0, p(A16), p(A16), None) == 1
+    assert f(p(A16), -1, 48, 8, p(A16), p(A16), None) == 1
+    assert f(p(0), 16, 48, 8, p(A16), p(A16), None) == 1
+    assert f(p(A16 + 2), 16, 48, 8, p(A16), p(A16), None) == 1      # alignment
+    assert f(p(0), 0, 48, 8, p(0), p(0), None) == 0                 # T == 0: nothing
 
 
 def test_moe_workspace_layout_is_consistent(nv):
