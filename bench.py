@@ -93,8 +93,13 @@ def make_weights(nv, cfg):
     return w13, w13sf, w13a, w2, w2sf, w2a
 
 
-def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True):
+def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=None):
     """Run warmup + timed steps; return (ms per step, per-stage ms, S_valid).
+
+    variant: None (the layer as specified), "static_x" (nvfp4_moe_forward_ex
+    with a static gs1, set to the value the dynamic rule gives for this x, so
+    the numbers are the same and only the amax pass is gone) or "per_half"
+    (w13 alphas of shape (E, 2), both halves equal to the per-expert alpha).
 
     events_in_loop: the stage events are recorded in every timed step (the
     per-stage device times then cover exactly the timed region). Otherwise
@@ -111,9 +116,15 @@ def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True):
     ws = torch.empty((nv.moe_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk),),
                      dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    x_gs = None
+    if variant == "static_x":
+        x_gs = nv.quantize(x)[2]
+    elif variant == "per_half":
+        w13, w13sf, w13a, w2, w2sf, w2a = weights
+        weights = (w13, w13sf, torch.stack([w13a, w13a], dim=1).contiguous(), w2, w2sf, w2a)
 
     def step(ev=None):
-        nv.moe_forward(x, ids, wts, *weights, y=y, workspace=ws, stage_events=ev)
+        nv.moe_forward(x, ids, wts, *weights, y=y, workspace=ws, stage_events=ev, x_gs=x_gs)
 
     for _ in range(warmup):
         step()
@@ -133,6 +144,28 @@ def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True):
     stage_ms = {k: float(np.mean([p[k] for p in per])) for k in per[0]}
     ok = bool(torch.isfinite(y.float()).all().item())
     return (t1 - t0) * 1e3 / steps, stage_ms, s_valid, ids_np, ok
+
+
+def time_router(nv, cfg, launches=200):
+    """Microseconds per nvfp4_route_topk launch on the config's logits (T, E),
+    top-k, timed with events on torch's current stream (the one the binding
+    launches on)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    rng = np.random.default_rng(cfg.seed_x)
+    logits = to_dev((rng.standard_normal((cfg.T, cfg.E)) + W.zipf_bias(cfg)[None, :]).astype(np.float32))
+    ids = torch.empty((cfg.T, cfg.topk), dtype=torch.int32, device="cuda")
+    wts = torch.empty((cfg.T, cfg.topk), dtype=torch.float32, device="cuda")
+    for _ in range(10):
+        nv.route_topk(logits, cfg.topk, ids, wts)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        nv.route_topk(logits, cfg.topk, ids, wts)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / launches
 
 
 def decode_bytes(cfg, ids_np):
@@ -283,6 +316,12 @@ def main():
         "note": "the source pages publish no throughput figures, only correctness traces on "
                 "their own (NVIDIA) hardware",
     }
+    # extensions beyond the five stages, measured on the same prefill batch
+    ext = {"router_us": {c.name: time_router(nv, c) for c in (W.PREFILL, W.SKEWED)}}
+    for variant in ("static_x", "per_half"):
+        vms, vstage, _, _, vfin = time_layer(nv, cfg, weights, 10, 3, variant=variant)
+        ext[variant] = {"ms_per_step": vms, "stage_ms": vstage, "finite": vfin}
+    out["extensions"] = ext
     if not args.no_decode:
         dcfg = W.DECODE
         dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, args.decode_steps, 5,

@@ -113,268 +113,287 @@ void gemm_kernel(GemmParams p) {
         row_start = t.row_start;
         row_count = t.row_count;
     }
+    // Each wave covers MI blocks of 32 rows, so a tile computes 64 * MI rows:
+    // the last tile of an expert usually holds fewer than 256 (at the prefill
+    // shape about 171 of 256 on average), and its MFMAs shrink with it. The
+    // loads still bring in all 256 rows (the extra ones repeat a valid row).
+    const int mi_tile = __builtin_amdgcn_readfirstlane((row_count + 63) / 64);
+    __shared__ uint32_t red[NT / 64];
+    auto tile = [&](auto mi_c) {
+        constexpr int MI = decltype(mi_c)::value;
+        // VALU per MFMA in the substeps' schedules: the dequant of one
+        // substep is about 11 VALU per operand (MI + 4 operands) spread over
+        // its 4 * MI MFMAs; the last substep's first kFirst MFMAs cover the
+        // fragment reads
+        constexpr int kValu = MI == 4 ? 5 : MI == 3 ? 6 : MI == 2 ? 8 : 14;
+        constexpr int kFirst = MI == 1 ? 2 : 6;
+        constexpr int kValuLast = MI == 4 ? 8 : MI == 3 ? 13 : MI == 2 ? 33 : 28;
 
-    // ---- buffer resources and per-lane DMA offsets ---------------------------
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aq, p.a_rows * ldq);
-    const __amdgpu_buffer_rsrc_t rasf = make_rsrc(p.asf, p.a_rows * ldsf);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
-    const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldwsf, N * ldwsf);
+        // ---- buffer resources and per-lane DMA offsets ---------------------------
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aq, p.a_rows * ldq);
+        const __amdgpu_buffer_rsrc_t rasf = make_rsrc(p.asf, p.a_rows * ldsf);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
+        const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldwsf, N * ldwsf);
 
-    auto a_src = [&](int r) -> int64_t {        // A tensor row of tile row r
-        int64_t src = row_start + (r < row_count ? r : 0);
-        if (MODE == kGemmL1) src = p.a_gather[src] / p.topk;
-        return src;
-    };
-    auto b_src = [&](int vc) -> int64_t {       // weight row (output column) of virtual column vc
-        if (MODE == kGemmL1) {
-            const int w = vc >> 7, r = vc & 127;
-            const int64_t base = (int64_t)nt * 128 + 64 * w + (r & 63);
-            if (base >= p.I) return 0;
-            return (r < 64) ? base : p.I + base;
+        auto a_src = [&](int r) -> int64_t {        // A tensor row of tile row r
+            int64_t src = row_start + (r < row_count ? r : 0);
+            if (MODE == kGemmL1) src = p.a_gather[src] / p.topk;
+            return src;
+        };
+        auto b_src = [&](int vc) -> int64_t {       // weight row (output column) of virtual column vc
+            if (MODE == kGemmL1) {
+                const int w = vc >> 7, r = vc & 127;
+                const int64_t base = (int64_t)nt * 128 + 64 * w + (r & 63);
+                if (base >= p.I) return 0;
+                return (r < 64) ? base : p.I + base;
+            }
+            const int64_t c = (int64_t)nt * BN + vc;
+            return c < N ? c : 0;
+        };
+        // data: wave w, instruction t (0..3) fills LDS slots (4w + t) * 64 + lane of
+        // 16 bytes: row (4w + t) * 16 + lane / 4, physical chunk lane & 3
+        uint32_t a_off[4], b_off[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int row = (4 * wave + t) * 16 + (lane >> 2);
+            const int chunk = swz(row, lane & 3);
+            a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
+            b_off[t] = (uint32_t)(wq_row(b_src(row), ldq) + 16 * chunk);
         }
-        const int64_t c = (int64_t)nt * BN + vc;
-        return c < N ? c : 0;
-    };
-    // data: wave w, instruction t (0..3) fills LDS slots (4w + t) * 64 + lane of
-    // 16 bytes: row (4w + t) * 16 + lane / 4, physical chunk lane & 3
-    uint32_t a_off[4], b_off[4];
+        // A scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 +
+        // lane: row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the
+        // step's 8. B scales: instruction t (0..3) fills dword (4w + t) * 64 + lane
+        // with pair lane & 3 of row (4w + t) * 16 + lane / 4.
+        uint32_t asf_off[2], bsf_off[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int row = (4 * wave + t) * 16 + (lane >> 2);
-        const int chunk = swz(row, lane & 3);
-        a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
-        b_off[t] = (uint32_t)(wq_row(b_src(row), ldq) + 16 * chunk);
-    }
-    // A scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 +
-    // lane: row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the
-    // step's 8. B scales: instruction t (0..3) fills dword (4w + t) * 64 + lane
-    // with pair lane & 3 of row (4w + t) * 16 + lane / 4.
-    uint32_t asf_off[2], bsf_off[4];
+        for (int t = 0; t < 2; ++t) {
+            const int row = (2 * wave + t) * 32 + (lane >> 1);
+            asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
+        }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int row = (2 * wave + t) * 32 + (lane >> 1);
-        asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-        bsf_off[t] = (uint32_t)wsf_off(b_src((4 * wave + t) * 16 + (lane >> 2)), ldwsf, 0, lane & 3);
+        for (int t = 0; t < 4; ++t)
+            bsf_off[t] = (uint32_t)wsf_off(b_src((4 * wave + t) * 16 + (lane >> 2)), ldwsf, 0, lane & 3);
 
-    const int nk = (int)(ldq / KB);
-    // part t (0..5) of the DMA of stage ks: t < 4 one A and one B data load,
-    // t = 4, 5 one A and two B scale loads
-    auto issue_part = [&](int ks, int t) {
-        uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-        // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
-        const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
-        const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)((ks >> 2) * kWsfQuad + (ks & 3) * 2);
-        if (t < 4) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
-                                                     16, a_off[t], kda, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
-                                                     16, b_off[t], kdb, 0, 0);
-        } else {
-            const int u = t - 4;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + u) * 256), 4, asf_off[u], ksa, 0, 0);
-#pragma unroll
-            for (int v = 2 * u; v < 2 * u + 2; ++v)
+        const int nk = (int)(ldq / KB);
+        // part t (0..5) of the DMA of stage ks: t < 4 one A and one B data load,
+        // t = 4, 5 one A and two B scale loads
+        auto issue_part = [&](int ks, int t) {
+            uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
+            // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
+            const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
+            const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)((ks >> 2) * kWsfQuad + (ks & 3) * 2);
+            if (t < 4) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
+                                                         16, a_off[t], kda, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
+                                                         16, b_off[t], kdb, 0, 0);
+            } else {
+                const int u = t - 4;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (4 * wave + v) * 256), 2,
-                    bsf_off[v], ksb, 0, 0);
-        }
-    };
-    auto issue_stage = [&](int ks) {
+                    rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + u) * 256), 4, asf_off[u], ksa, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 6; ++t) issue_part(ks, t);
-    };
+                for (int v = 2 * u; v < 2 * u + 2; ++v)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (4 * wave + v) * 256), 2,
+                        bsf_off[v], ksb, 0, 0);
+            }
+        };
+        auto issue_stage = [&](int ks) {
+#pragma unroll
+            for (int t = 0; t < 6; ++t) issue_part(ks, t);
+        };
 
-    // ---- main loop ---------------------------------------------------------
-    const int wm = wave >> 1, wn = wave & 1;
-    const int l32 = lane & 31, h = lane >> 5;
+        // ---- main loop ---------------------------------------------------------
+        const int wm = wave >> 1, wn = wave & 1;
+        const int l32 = lane & 31, h = lane >> 5;
 
-    float16_t acc[4][4];
+        float16_t acc[MI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    u32x4 fa[4][2], fb[4][2];
-    uint32_t sa[4], sb[4];
-    auto read_frags = [&](int ks) {
-        const uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-        const uint8_t* sA = base;
-        const uint8_t* sB = base + A_BYTES;
-        const uint8_t* sAsf = base + A_BYTES + B_BYTES;
-        const uint8_t* sBsf = sAsf + ASF_BYTES;
+        u32x4 fa[MI][2], fb[4][2];
+        uint32_t sa[MI], sb[4];
+        auto read_frags = [&](int ks) {
+            const uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
+            const uint8_t* sA = base;
+            const uint8_t* sB = base + A_BYTES;
+            const uint8_t* sAsf = base + A_BYTES + B_BYTES;
+            const uint8_t* sBsf = sAsf + ASF_BYTES;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + 32 * i + l32;
-            fa[i][0] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h));
-            fa[i][1] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h + 1));
-            sa[i] = *reinterpret_cast<const uint32_t*>(sAsf + row * 8 + 4 * h);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int vc = wn * 128 + 32 * j + l32;
-            fb[j][0] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h));
-            fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
-            // pairs 2h and 2h + 1, each in the low half of its dword
-            const u32x2 d = *reinterpret_cast<const u32x2*>(sBsf + vc * 16 + 8 * h);
-            sb[j] = d[0] | (d[1] << 16);
-        }
-    };
-    // operands of substep s in registers s & 1
-    half8_t ha[2][4], hb[2][4];
-    auto deq = [&](int s, half8_t (&xa)[4], half8_t (&xb)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
-    };
-
-    // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
-    // substep s issues its 16 MFMAs with the dequant of substep s + 1 between
-    // them. Substep 7 starts with the wait for this wave's DMA of stage ks+1
-    // and the barrier (the other waves' DMA of it is then visible, and buffer
-    // (ks-1) % 4, which the next step refills, has been read by everyone),
-    // reads the fragments of step ks+1, and dequantizes substep 0 of step ks+1
-    // between its later MFMAs, so that no dequant runs outside an MFMA shadow.
-    // Scheduling barriers keep each substep's instructions together.
-    for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    read_frags(0);
-    deq(0, ha[0], hb[0]);
-
-    // One K step. Phase 0: steady state (refill a stage, wait until 28 loads
-    // remain, fetch the next step); 1 and 2: the last two refills have been
-    // issued (wait until 14 / 0 remain); 3: the last step. Every condition is a
-    // compile-time constant, so a step is one basic block the scheduler can
-    // interleave freely.
-    auto step = [&](int ks, auto mode_c) {
-        constexpr int PH = decltype(mode_c)::value;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            // the refill of stage ks+3 is spread over substeps 0..5: a burst of
-            // fourteen LDS-DMA issues at once stalls the MFMA stream
-            if (PH == 0 && s < 6) issue_part(ks + NSTAGE - 1, s);
-            if (s < 7) {
-                deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
-            } else if (PH < 3) {
-                // this wave's DMA of stage ks+1 is done when at most the stages
-                // issued after it are outstanding; lgkmcnt(0): its own fragment
-                // reads of this step are complete before it passes the barrier
-                if (PH == 0) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
-                if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007E);        // vmcnt(14) lgkmcnt(0)
-                if (PH == 2) __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
-                lds_barrier();
-                read_frags(ks + 1);
+            for (int i = 0; i < MI; ++i) {
+                const int row = wm * (32 * MI) + 32 * i + l32;
+                fa[i][0] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h));
+                fa[i][1] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h + 1));
+                sa[i] = *reinterpret_cast<const uint32_t*>(sAsf + row * 8 + 4 * h);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[s & 1][i], hb[s & 1][j],
-                                                                        acc[i][j], 0, 0, 0);
-            if (s < 7) {
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);       // five VALU
-                }
-            } else if (PH < 3) {
-                deq(0, ha[0], hb[0]);
-                // the fragment reads land under the first MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);          // the LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-#pragma unroll
-                for (int k = 0; k < 10; ++k) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const int vc = wn * 128 + 32 * j + l32;
+                fb[j][0] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h));
+                fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
+                // pairs 2h and 2h + 1, each in the low half of its dword
+                const u32x2 d = *reinterpret_cast<const u32x2*>(sBsf + vc * 16 + 8 * h);
+                sb[j] = d[0] | (d[1] << 16);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    int ks = 0;
-    for (; ks + NSTAGE - 1 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
-    if (nk - ks == 3) step(ks++, std::integral_constant<int, 1>{});
-    if (nk - ks == 2) step(ks++, std::integral_constant<int, 2>{});
-    step(ks, std::integral_constant<int, 3>{});
-    __syncthreads();
+        };
+        // operands of substep s in registers s & 1
+        half8_t ha[2][MI], hb[2][4];
+        auto deq = [&](int s, half8_t (&xa)[MI], half8_t (&xb)[4]) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
+        };
 
-    // ---- epilogue ------------------------------------------------------------
-    // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
-    // L1 with per-half weight scales: gate columns take alpha, up alpha_up
-    const int ast = (MODE == kGemmL1 && p.alpha_stride > 1) ? 2 : 1;
-    const float alpha = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast];
-    if (MODE == kGemmL1) {
-        const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
-        // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
-        // The rounded (gate, up) pairs of one half of the tile (128 rows x 128
-        // act columns) go through the now idle LDS; then all threads apply
-        // SiLU and store act row by row (coalesced), in two halves.
-        uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [128][128] g | u << 16
-        uint32_t amax_bits = 0;
-        for (int half = 0; half < 2; ++half) {
-            if (wm == half) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const int col = wn * 64 + 32 * j + l32;
-                            const uint32_t g = f32_to_bf16_rne(alpha * acc[i][j][r]);
-                            const uint32_t u = f32_to_bf16_rne(alpha_up * acc[i][j + 2][r]);
-                            gu[row * 128 + col] = g | (u << 16);
-                        }
-            }
-            __syncthreads();
-            for (int e = tid; e < 128 * 128; e += NT) {
-                const int local = half * 128 + (e >> 7);
-                const int64_t col = (int64_t)nt * 128 + (e & 127);
-                if (local < row_count && col < p.I) {
-                    const uint32_t w = gu[e];
-                    const uint32_t a = silu_mul_bf16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
-                    p.out_bf16[(int64_t)(row_start + local) * p.I + col] = (uint16_t)a;
-                    amax_bits = max(amax_bits, a & 0x7FFFu);
-                }
-            }
-            __syncthreads();
-        }
-        __shared__ uint32_t red[NT / 64];
-        amax_bits = wave_max_u32(amax_bits);
-        if (lane == 0) red[wave] = amax_bits;
+        // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
+        // substep s issues its 16 MFMAs with the dequant of substep s + 1 between
+        // them. Substep 7 starts with the wait for this wave's DMA of stage ks+1
+        // and the barrier (the other waves' DMA of it is then visible, and buffer
+        // (ks-1) % 4, which the next step refills, has been read by everyone),
+        // reads the fragments of step ks+1, and dequantizes substep 0 of step ks+1
+        // between its later MFMAs, so that no dequant runs outside an MFMA shadow.
+        // Scheduling barriers keep each substep's instructions together.
+        for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid == 0) {
-            uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
-            atomicMax(p.amax_slot, m << 16);
-        }
-    } else {
+        read_frags(0);
+        deq(0, ha[0], hb[0]);
+
+        // One K step. Phase 0: steady state (refill a stage, wait until 28 loads
+        // remain, fetch the next step); 1 and 2: the last two refills have been
+        // issued (wait until 14 / 0 remain); 3: the last step. Every condition is a
+        // compile-time constant, so a step is one basic block the scheduler can
+        // interleave freely.
+        auto step = [&](int ks, auto mode_c) {
+            constexpr int PH = decltype(mode_c)::value;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int s = 0; s < 8; ++s) {
+                // the refill of stage ks+3 is spread over substeps 0..5: a burst of
+                // fourteen LDS-DMA issues at once stalls the MFMA stream
+                if (PH == 0 && s < 6) issue_part(ks + NSTAGE - 1, s);
+                if (s < 7) {
+                    deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
+                } else if (PH < 3) {
+                    // this wave's DMA of stage ks+1 is done when at most the stages
+                    // issued after it are outstanding; lgkmcnt(0): its own fragment
+                    // reads of this step are complete before it passes the barrier
+                    if (PH == 0) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
+                    if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007E);        // vmcnt(14) lgkmcnt(0)
+                    if (PH == 2) __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
+                    lds_barrier();
+                    read_frags(ks + 1);
+                }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int local = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (local >= row_count) continue;
-                const int64_t prow = row_start + local;
+                for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + l32;
-                    if (col >= N) continue;
-                    const float v = alpha * acc[i][j][r];
-                    if (MODE == kGemmL2) p.out_f32[prow * N + col] = v;
-                    else p.out_bf16[prow * N + col] = (uint16_t)f32_to_bf16_rne(v);
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[s & 1][i], hb[s & 1][j],
+                                                                            acc[i][j], 0, 0, 0);
+                if (s < 7) {
+#pragma unroll
+                    for (int k = 0; k < 4 * MI; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);   // its VALU share
+                    }
+                } else if (PH < 3) {
+                    deq(0, ha[0], hb[0]);
+                    // the fragment reads land under the first MFMAs
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3 * MI + 12, 0);  // the LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x008, kFirst, 0);
+#pragma unroll
+                    for (int k = 0; k < 4 * MI - kFirst; ++k) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, kValuLast, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        int ks = 0;
+        for (; ks + NSTAGE - 1 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
+        if (nk - ks == 3) step(ks++, std::integral_constant<int, 1>{});
+        if (nk - ks == 2) step(ks++, std::integral_constant<int, 2>{});
+        step(ks, std::integral_constant<int, 3>{});
+        __syncthreads();
+
+        // ---- epilogue ------------------------------------------------------------
+        // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
+        // L1 with per-half weight scales: gate columns take alpha, up alpha_up
+        const int ast = (MODE == kGemmL1 && p.alpha_stride > 1) ? 2 : 1;
+        const float alpha = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast];
+        if (MODE == kGemmL1) {
+            const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
+            // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
+            // The rounded (gate, up) pairs of one half of the tile (128 rows x 128
+            // act columns) go through the now idle LDS; then all threads apply
+            // SiLU and store act row by row (coalesced), in two halves.
+            uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [128][128] g | u << 16
+            uint32_t amax_bits = 0;
+            for (int half = 0; half < 2; ++half) {
+                if (wm == half) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                                const int col = wn * 64 + 32 * j + l32;
+                                const uint32_t g = f32_to_bf16_rne(alpha * acc[i][j][r]);
+                                const uint32_t u = f32_to_bf16_rne(alpha_up * acc[i][j + 2][r]);
+                                gu[row * 128 + col] = g | (u << 16);
+                            }
+                }
+                __syncthreads();
+                for (int e = tid; e < 32 * MI * 128; e += NT) {
+                    const int local = half * (32 * MI) + (e >> 7);
+                    const int64_t col = (int64_t)nt * 128 + (e & 127);
+                    if (local < row_count && col < p.I) {
+                        const uint32_t w = gu[e];
+                        const uint32_t a = silu_mul_bf16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
+                        p.out_bf16[(int64_t)(row_start + local) * p.I + col] = (uint16_t)a;
+                        amax_bits = max(amax_bits, a & 0x7FFFu);
+                    }
+                }
+                __syncthreads();
+            }
+            amax_bits = wave_max_u32(amax_bits);
+            if (lane == 0) red[wave] = amax_bits;
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+                atomicMax(p.amax_slot, m << 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int local = wm * (32 * MI) + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if (local >= row_count) continue;
+                    const int64_t prow = row_start + local;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + l32;
+                        if (col >= N) continue;
+                        const float v = alpha * acc[i][j][r];
+                        if (MODE == kGemmL2) p.out_f32[prow * N + col] = v;
+                        else p.out_bf16[prow * N + col] = (uint16_t)f32_to_bf16_rne(v);
+                    }
                 }
             }
         }
-    }
+    };
+    if (mi_tile >= 4) tile(std::integral_constant<int, 4>{});
+    else if (mi_tile == 3) tile(std::integral_constant<int, 3>{});
+    else if (mi_tile == 2) tile(std::integral_constant<int, 2>{});
+    else tile(std::integral_constant<int, 1>{});
 }
 
 template <int MODE>

@@ -31,7 +31,8 @@ def _run(nv, aq, asf, ags, bq, bsf, balpha):
 
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 32, 384), (17, 272, 640), (256, 256, 256),
                                    (300, 512, 1024), (257, 48, 7168), (64, 6144, 128),
-                                   (513, 784, 896)])
+                                   (513, 784, 896), (160, 256, 512), (100, 512, 256),
+                                   (420, 384, 1024)])
 def test_gemm_random(nv, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     out = _run(nv, *ops)

@@ -231,3 +231,16 @@ def test_path_switch_boundary(nv, T):
     # S = 16 * E takes the weight-streaming kernels, one more slot the tiled GEMM
     cfg = W.small_layer(f"switch{T}", T=T, H=512, I=256, E=4, topk=2, seed=26 + T)
     compare_layer(nv, make_layer(cfg), f"path switch T={T}")
+
+
+def test_tile_row_block_variants(nv):
+    # the GEMM sizes each tile to 64-row multiples of its row count: experts
+    # with 427 (256 + 171), 150, 64 and 65 slots take tiles of 4, 3, 1 and 2
+    # row blocks per wave
+    counts = [427, 150, 64, 65]
+    T = sum(counts)
+    cfg = W.small_layer("mi", T=T, H=512, I=256, E=4, topk=1, seed=27)
+    L = make_layer(cfg)
+    L["ids"] = np.repeat(np.arange(4, dtype=np.int32), counts)[np.random.default_rng(27).permutation(T)][:, None]
+    g, _, _ = compare_layer(nv, L, "tile row-block variants")
+    assert list(g["counts"]) == counts
