@@ -80,14 +80,27 @@ __device__ __forceinline__ double exp_f64(double x) {
 // (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
 // about 1 in 256 of those products is a bf16 midpoint, which float32 alone
 // would round the wrong way.)
+// e^-|g| for |g| <= 87 (the result stays a normal float): the hardware base-2
+// exponential (1 ulp) of t = -|g| log2(e) rounded to float, times
+// 1 + (rest of the product) ln 2, which restores the bits lost in rounding t
+// (|rest| < 2^-17, so the linear term is exact to far below an ulp).
+__device__ __forceinline__ float exp_neg_abs(float g) {
+    const float a = -fabsf(g);
+    const float t = a * 1.44269502f;                                           // log2(e), head
+    const float rest = __builtin_fmaf(a, 1.44269502f, -t) + a * 1.925963e-8f; // tail of a log2(e)
+    const float p = __builtin_amdgcn_exp2f(t);
+    return __builtin_fmaf(p, rest * 0.693147182f, p);
+}
+
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
     if (g >= -87.0f) {
         // silu(g) = g / (1 + e^-g) = g e^g / (1 + e^g); one exponential of -|g|
-        // serves both signs. Error: expf and the fast division a couple of ulps
-        // each, the products half an ulp: well inside the 32-ulp margin below.
-        const float e = expf(-fabsf(g));
+        // serves both signs. Error: the exponential about 2 ulps, the
+        // hardware reciprocal 1 ulp, the sum and the three products half an
+        // ulp each: under 6 ulps, well inside the 32-ulp margin below.
+        const float e = exp_neg_abs(g);
         const float num = (g >= 0.0f) ? g : g * e;
-        const float v = __fdividef(num, 1.0f + e) * u;
+        const float v = num * __builtin_amdgcn_rcpf(1.0f + e) * u;
         const uint32_t b = __float_as_uint(v);
         const uint32_t low = b & 0xFFFFu;
         const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;

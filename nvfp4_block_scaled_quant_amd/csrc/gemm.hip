@@ -351,14 +351,25 @@ void gemm_kernel(GemmParams p) {
                             }
                 }
                 __syncthreads();
-                for (int e = tid; e < 32 * MI * 128; e += NT) {
-                    const int local = half * (32 * MI) + (e >> 7);
-                    const int64_t col = (int64_t)nt * 128 + (e & 127);
-                    if (local < row_count && col < p.I) {
-                        const uint32_t w = gu[e];
-                        const uint32_t a = silu_mul_bf16(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
-                        p.out_bf16[(int64_t)(row_start + local) * p.I + col] = (uint16_t)a;
-                        amax_bits = max(amax_bits, a & 0x7FFFu);
+                // each thread: one pair of adjacent act columns (one 4-byte
+                // store) in rows tid / 64, + 4, ...; a wave covers one row (256
+                // contiguous bytes), so the row bound is wave-uniform
+                {
+                    const int cp = tid & 63;
+                    const int64_t col = (int64_t)nt * 128 + 2 * cp;   // I is even: no pair straddles I
+                    if (col < p.I) {
+                        const int r0 = tid >> 6;
+                        uint32_t* dst = reinterpret_cast<uint32_t*>(
+                            p.out_bf16 + (int64_t)(row_start + half * (32 * MI) + r0) * p.I + col);
+                        const int64_t dstep = 2 * p.I;                // 4 rows, in 4-byte units
+                        for (int r = r0; r < 32 * MI && half * (32 * MI) + r < row_count;
+                             r += NT / 64, dst += dstep) {
+                            const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * 128 + 2 * cp);
+                            const uint32_t a0 = silu_mul_bf16(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16));
+                            const uint32_t a1 = silu_mul_bf16(bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
+                            *dst = a0 | (a1 << 16);
+                            amax_bits = max(amax_bits, max(a0 & 0x7FFFu, a1 & 0x7FFFu));
+                        }
                     }
                 }
                 __syncthreads();
