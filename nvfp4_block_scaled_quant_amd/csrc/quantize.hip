@@ -183,7 +183,10 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s) {
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* slot, hipStream_t s) {
     if (n <= 0) return hipSuccess;
-    const int g = grid_for(n / 8, 2048);
+    // at most 256 work-groups: every work-group ends with one atomic on the
+    // same slot, and those serialize (about 10 ns each, measured: 2048
+    // work-groups took 29.6 us for 58.7 MB, 256 took 12.3 us)
+    const int g = grid_for(n / 8, 256);
     amax_kernel<<<dim3(g, 1), kThreads, 0, s>>>(x, n, slot);
     return hipGetLastError();
 }
