@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Two float32 -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// one hardware conversion on gfx950 (finite inputs give the same bits as
+// f32_to_bf16_rne).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // float64 -> bf16 bits, nearest-even, in effect one rounding: rounding to
 // float32 toward zero and setting the last bit when inexact (round to odd)
 // keeps enough information for the second rounding to be exact.
@@ -72,14 +81,6 @@ __device__ __forceinline__ double exp_f64(double x) {
     return __builtin_ldexp(p, (int)n);
 }
 
-// act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
-// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
-// A float32 evaluation (relative error a few ulps) decides the rounding when
-// it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
-// e^g leaves the float32 normal range, the product is recomputed in float64.
-// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
-// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
-// would round the wrong way.)
 // e^-|g| for |g| <= 87 (the result stays a normal float): the hardware base-2
 // exponential (1 ulp) of t = -|g| log2(e) rounded to float, times
 // 1 + (rest of the product) ln 2, which restores the bits lost in rounding t
@@ -92,21 +93,30 @@ __device__ __forceinline__ float exp_neg_abs(float g) {
     return __builtin_fmaf(p, rest * 0.693147182f, p);
 }
 
+// act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
+// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
+// A float32 evaluation (relative error a few ulps) decides the rounding when
+// it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
+// e^g leaves the float32 normal range, the product is recomputed in float64.
+// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
+// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
+// would round the wrong way.)
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
-    if (g >= -87.0f) {
-        // silu(g) = g / (1 + e^-g) = g e^g / (1 + e^g); one exponential of -|g|
-        // serves both signs. Error: the exponential about 2 ulps, the
-        // hardware reciprocal 1 ulp, the sum and the three products half an
-        // ulp each: under 6 ulps, well inside the 32-ulp margin below.
-        const float e = exp_neg_abs(g);
-        const float num = (g >= 0.0f) ? g : g * e;
-        const float v = num * __builtin_amdgcn_rcpf(1.0f + e) * u;
-        const uint32_t b = __float_as_uint(v);
-        const uint32_t low = b & 0xFFFFu;
-        const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
-        if ((b & 0x7F800000u) != 0u && (b & 0x7F800000u) != 0x7F800000u && dist > 32u)
-            return f32_to_bf16_rne(v);
-    }
+    // silu(g) = g / (1 + e^-g) = g e^g / (1 + e^g); one exponential of -|g|
+    // serves both signs. Error: the exponential about 2 ulps, the hardware
+    // reciprocal 1 ulp, the sum and the three products half an ulp each:
+    // under 6 ulps, well inside the 32-ulp margin below. Computed without
+    // branches (g clamped to -87 for the exponential); the float64 path is
+    // the only branch.
+    const float e = exp_neg_abs(fmaxf(g, -87.0f));
+    const float num = (g >= 0.0f) ? g : g * e;
+    const float v = num * __builtin_amdgcn_rcpf(1.0f + e) * u;
+    const uint32_t b = __float_as_uint(v);
+    const uint32_t low = b & 0xFFFFu;
+    const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
+    const uint32_t ex = b & 0x7F800000u;
+    const bool ok = (g >= -87.0f) & (ex != 0u) & (ex != 0x7F800000u) & (dist > 32u);
+    if (__builtin_expect(ok, 1)) return f32_to_bf16_rne(v);
     const double gd = g, ud = u;
     return f64_to_bf16_rne((gd / (1.0 + exp_f64(-gd))) * ud);
 }

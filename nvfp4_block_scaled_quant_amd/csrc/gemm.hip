@@ -330,49 +330,48 @@ void gemm_kernel(GemmParams p) {
         if (MODE == kGemmL1) {
             const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
             // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
-            // The rounded (gate, up) pairs of one half of the tile (128 rows x 128
-            // act columns) go through the now idle LDS; then all threads apply
-            // SiLU and store act row by row (coalesced), in two halves.
-            uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [128][128] g | u << 16
+            // All four waves stage the rounded (gate, up) pairs of the whole
+            // tile (64 * MI rows x 128 act columns) in the now idle LDS, rows
+            // padded to 130 words (the two lane halves' rows, four apart, then
+            // fall in different banks; 8-byte reads stay aligned); then all
+            // threads apply SiLU and store act row by row (coalesced).
+            constexpr int GU_LD = 130;
+            static_assert(64 * MI * GU_LD * 4 <= LDS_BYTES, "gate/up staging fits in LDS");
+            uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [64 MI][GU_LD] g | u << 16
             uint32_t amax_bits = 0;
-            for (int half = 0; half < 2; ++half) {
-                if (wm == half) {
 #pragma unroll
-                    for (int i = 0; i < MI; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
+                for (int r = 0; r < 16; ++r)
 #pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                const int row = 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                                const int col = wn * 64 + 32 * j + l32;
-                                const uint32_t g = f32_to_bf16_rne(alpha * acc[i][j][r]);
-                                const uint32_t u = f32_to_bf16_rne(alpha_up * acc[i][j + 2][r]);
-                                gu[row * 128 + col] = g | (u << 16);
-                            }
-                }
-                __syncthreads();
-                // each thread: one pair of adjacent act columns (one 4-byte
-                // store) in rows tid / 64, + 4, ...; a wave covers one row (256
-                // contiguous bytes), so the row bound is wave-uniform
-                {
-                    const int cp = tid & 63;
-                    const int64_t col = (int64_t)nt * 128 + 2 * cp;   // I is even: no pair straddles I
-                    if (col < p.I) {
-                        const int r0 = tid >> 6;
-                        uint32_t* dst = reinterpret_cast<uint32_t*>(
-                            p.out_bf16 + (int64_t)(row_start + half * (32 * MI) + r0) * p.I + col);
-                        const int64_t dstep = 2 * p.I;                // 4 rows, in 4-byte units
-                        for (int r = r0; r < 32 * MI && half * (32 * MI) + r < row_count;
-                             r += NT / 64, dst += dstep) {
-                            const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * 128 + 2 * cp);
-                            const uint32_t a0 = silu_mul_bf16(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16));
-                            const uint32_t a1 = silu_mul_bf16(bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
-                            *dst = a0 | (a1 << 16);
-                            amax_bits = max(amax_bits, max(a0 & 0x7FFFu, a1 & 0x7FFFu));
-                        }
+                    for (int j = 0; j < 2; ++j) {
+                        const int row = wm * (32 * MI) + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                        const int col = wn * 64 + 32 * j + l32;
+                        gu[row * GU_LD + col] = pack_bf16x2_rne(alpha * acc[i][j][r], alpha_up * acc[i][j + 2][r]);
+                    }
+            __syncthreads();
+            // each thread: one pair of adjacent act columns (one 4-byte store)
+            // in rows tid / 64, + 4, ...; a wave covers one row (256 contiguous
+            // bytes), so the row bound is wave-uniform
+            {
+                const int cp = tid & 63;
+                const int64_t col = (int64_t)nt * 128 + 2 * cp;   // I is even: no pair straddles I
+                if (col < p.I) {
+                    const int r0 = tid >> 6;
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(p.out_bf16 + (int64_t)(row_start + r0) * p.I + col);
+                    const int64_t dstep = 2 * p.I;                // 4 rows, in 4-byte units
+                    const int rows = min(row_count, 64 * MI);
+                    // unrolled: the LDS reads of four rows are in flight together
+                    // (one wave per SIMD has nothing else to hide their latency)
+#pragma unroll 4
+                    for (int r = r0; r < rows; r += NT / 64, dst += dstep) {
+                        const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * GU_LD + 2 * cp);
+                        const uint32_t a0 = silu_mul_bf16(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16));
+                        const uint32_t a1 = silu_mul_bf16(bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
+                        *dst = a0 | (a1 << 16);
+                        amax_bits = max(amax_bits, max(a0 & 0x7FFFu, a1 & 0x7FFFu));
                     }
                 }
-                __syncthreads();
             }
             amax_bits = wave_max_u32(amax_bits);
             if (lane == 0) red[wave] = amax_bits;
