@@ -380,6 +380,47 @@ void gemm_kernel(GemmParams p) {
                 uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
                 atomicMax(p.amax_slot, m << 16);
             }
+        } else if (MODE == kGemmL2) {
+            // A lane holds four consecutive rows of one column per group of
+            // four accumulator registers. A 4 x 4 transpose inside each quad of
+            // lanes (two butterfly stages of quad-permute DPP moves) gives lane
+            // 4c + m row m of that group at columns 4c .. 4c + 3, so every
+            // store writes 16 contiguous bytes: 64 stores per lane instead of
+            // 256 (the per-wave limit of 63 outstanding memory operations
+            // otherwise stalls the epilogue on store latency several times).
+            const int m = l32 & 3;
+            const bool odd = (m & 1) != 0, upper = (m & 2) != 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int local = wm * (32 * MI) + 32 * i + 8 * g + 4 * h + m;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v0 = alpha * acc[i][j][4 * g], v1 = alpha * acc[i][j][4 * g + 1];
+                        float v2 = alpha * acc[i][j][4 * g + 2], v3 = alpha * acc[i][j][4 * g + 3];
+                        // stage 1 (lanes m, m ^ 1): even lanes take the partner's
+                        // v0 / v2 into v1 / v3, odd lanes its v1 / v3 into v0 / v2
+                        const float s1a = odd ? v0 : v1, s1b = odd ? v2 : v3;
+                        const float r1a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s1a), 0xB1, 0xF, 0xF, false));   // quad_perm(1,0,3,2)
+                        const float r1b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s1b), 0xB1, 0xF, 0xF, false));
+                        if (odd) { v0 = r1a; v2 = r1b; } else { v1 = r1a; v3 = r1b; }
+                        // stage 2 (lanes m, m ^ 2): pairs (v0, v1) <-> (v2, v3)
+                        const float s2a = upper ? v0 : v2, s2b = upper ? v1 : v3;
+                        const float r2a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s2a), 0x4E, 0xF, 0xF, false));   // quad_perm(2,3,0,1)
+                        const float r2b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s2b), 0x4E, 0xF, 0xF, false));
+                        if (upper) { v0 = r2a; v1 = r2b; } else { v2 = r2a; v3 = r2b; }
+                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + 4 * (l32 >> 2);
+                        if (local < row_count && col < N)   // N % 16 == 0: four columns are in or out together
+                            *reinterpret_cast<float4_t*>(p.out_f32 + (row_start + local) * N + col) =
+                                (float4_t){v0, v1, v2, v3};
+                    }
+                }
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
