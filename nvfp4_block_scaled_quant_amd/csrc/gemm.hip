@@ -107,8 +107,13 @@ void gemm_kernel(GemmParams p) {
         row_count = (int)min((int64_t)BM, p.M - row_start);
         if (row_count <= 0) return;
     } else {
-        if (tile_idx >= *p.num_tiles) return;
+        // both loads at once (tile_idx < max_tiles: the entry exists, and is
+        // used only when it is one of the num_tiles valid ones)
         const Tile t = p.tiles[tile_idx];
+        const int ntiles = *p.num_tiles;
+        // keeps the tile load above the branch (the compiler would sink it)
+        asm volatile("" ::"s"(t.expert), "s"(t.row_start), "s"(t.row_count));
+        if (tile_idx >= ntiles) return;
         expert = t.expert;
         row_start = t.row_start;
         row_count = t.row_count;
@@ -260,8 +265,12 @@ void gemm_kernel(GemmParams p) {
         // between its later MFMAs, so that no dequant runs outside an MFMA shadow.
         // Scheduling barriers keep each substep's instructions together.
         for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // only stage 0 is needed now: wait until the later stages' loads are
+        // all that is outstanding (14 per stage), not for all of them
+        if (nk >= 3) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
+        else if (nk == 2) __builtin_amdgcn_s_waitcnt(0x007E);   // vmcnt(14) lgkmcnt(0)
+        else __builtin_amdgcn_s_waitcnt(0x0070);                // vmcnt(0) lgkmcnt(0)
+        lds_barrier();
         read_frags(0);
         deq(0, ha[0], hb[0]);
 

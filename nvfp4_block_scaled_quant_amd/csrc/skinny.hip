@@ -73,8 +73,13 @@ void skinny_kernel(GemmParams p) {
     const int nslab = (int)skinny_slabs(MODE, p.I, N);
     const int tile_idx = blockIdx.x / nslab;
     const int slab = blockIdx.x - tile_idx * nslab;
-    if (tile_idx >= *p.num_tiles) return;
+    // both loads at once (tile_idx < max_tiles: the entry exists, and is used
+    // only when it is one of the num_tiles valid ones)
     const Tile tl = p.tiles[tile_idx];
+    const int ntiles = *p.num_tiles;
+    // keeps the tile load above the branch (the compiler would sink it)
+    asm volatile("" ::"s"(tl.expert), "s"(tl.row_start), "s"(tl.row_count));
+    if (tile_idx >= ntiles) return;
     // the tile is the same for the whole work-group: keep its fields scalar, so
     // that the weight buffer descriptors are uniform
     const int expert = __builtin_amdgcn_readfirstlane(tl.expert);
