@@ -204,8 +204,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
-// One thread per 8 consecutive columns of one token; `chunks` work-groups of
-// 256 threads per token.
+// One thread per 4 consecutive columns of one token; `chunks` blocks of 256
+// threads (1,024 columns) per token.
 __device__ __forceinline__ void combine_block(const float* __restrict__ o2,
                                               const int32_t* __restrict__ slot_row,
                                               const float* __restrict__ weights, int topk, int64_t H,
