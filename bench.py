@@ -251,8 +251,8 @@ def calibrate_copy():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the layer is measured on one GPU's share of experts)", file=sys.stderr)
+        print(f"bench.py: the layer is measured on one GPU's share of experts; --gpus {args.gpus} "
+              f"is not supported (only --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

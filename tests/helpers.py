@@ -1,6 +1,6 @@
 """Comparison helpers for GPU-vs-oracle parity tests.
 
-Tolerance reading (the benchmark spec: GEMM and layer outputs within a max relative
+Tolerance reading (the target tolerance: GEMM and layer outputs within a max relative
 error of 2e-3 of the oracle's fp64 accumulation, cosine >= 0.9999). A bf16
 output carries its own rounding of up to half an ulp, which is up to 2^-8 ~
 3.9e-3 of an element just above a power of two, so no bf16 output can meet a
@@ -18,7 +18,7 @@ import numpy as np
 
 from oracle.formats import bf16_from_f64, bf16_to_f32
 
-NORTH_STAR_TOL = 2e-3
+REL_TOL = 2e-3
 MIN_SUB = 2.0 ** -133
 
 
@@ -40,9 +40,9 @@ def bf16_neighbors(bits):
     return down, up
 
 
-def check_bf16_output(gpu_bits, ref, name="out", tol=NORTH_STAR_TOL, faithful_floor=2.0 ** -6,
+def check_bf16_output(gpu_bits, ref, name="out", tol=REL_TOL, faithful_floor=2.0 ** -6,
                       min_exact=0.99, faithful_rows=None, bound_rows=None, amax=None):
-    """Assert the benchmark spec bound (as read above) on `bound_rows` of the first
+    """Assert the 2e-3 bound (as read above) on `bound_rows` of the first
     axis (all rows by default), faithful rounding for non-tiny elements of
     `faithful_rows`, and a high exact-match rate; return a stats dict. `amax`
     overrides max|ref| as the normalizer (when a subset of rows is checked)."""

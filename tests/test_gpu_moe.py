@@ -75,7 +75,7 @@ def compare_layer(nv, L, label, min_act_exact=0.995, pool=None):
 
     # stage 5: y. Tokens whose slots' quantized act rows (bytes and scale
     # bytes) all equal the oracle's, with the same gs2, feed identical inputs
-    # to L2 and the combine, so their y is unique: the benchmark spec bound and
+    # to L2 and the combine, so their y is unique: the 2e-3 bound and
     # faithful rounding apply. Where a gate/up value sits within float32
     # accumulation noise of a bf16 midpoint both roundings are valid; a
     # resulting flipped requantized nibble moves y by up to a few 1e-3 of
