@@ -252,8 +252,9 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  * hipEventElapsedTime(ev[i], ev[i+1]) is stage i's device time.
  * ------------------------------------------------------------------------ */
 enum {
-    NVFP4_MOE_STAGE_ROUTE = 0,      /* routing tables, tile list */
-    NVFP4_MOE_STAGE_QUANT_X = 1,    /* amax + quantization of x */
+    NVFP4_MOE_STAGE_ROUTE = 0,      /* amax of x, then routing tables, tile list
+                                       and the quantization of x (one launch) */
+    NVFP4_MOE_STAGE_QUANT_X = 1,    /* empty: x is quantized with the routing */
     NVFP4_MOE_STAGE_L1 = 2,         /* L1 grouped GEMM + fused SiLU*up */
     NVFP4_MOE_STAGE_REQUANT = 3,    /* quantization of act */
     NVFP4_MOE_STAGE_L2 = 4,         /* L2 grouped GEMM */

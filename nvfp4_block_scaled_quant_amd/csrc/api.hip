@@ -336,22 +336,22 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
         return stage_events ? hipEventRecord(stage_events[i], stream) : hipSuccess;
     };
 
-    // 1. routing tables + tile list (also zeroes both amax slots)
+    // 1 + 2. routing tables + tile list, and the quantization of x in further
+    // work-groups of the same launch, concurrently with the routing (stage 2
+    // is then empty). A larger x (and no static scale) first gets its amax
+    // from the amax kernel; a small one is reduced by the quantization
+    // work-groups themselves. The routing launch zeroes the act amax slot.
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_ROUTE));
-    // A small x is quantized by a second work-group of the routing launch
-    // (stage 2 is then empty); a larger one by the amax and block kernels.
     const bool small_x = T * H <= kSmallQuantMax;
-    const SmallQuant sq = {x, x_gs, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
-    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
-                           slot_row, tiles, num_tiles, amax, 2, small_x ? &sq : nullptr, stream));
-    // 2. quantize x
-    NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
-    if (!small_x) {
-        // a static global scale (x_gs) needs no amax pass
-        if (!x_gs) NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
-        NVFP4_TRY(launch_quant_rows(x, T, H, nullptr, amax, xq, pitch_q(H), xsf, pitch_sf(H), gs1,
-                                    stream, x_gs));
+    const bool amax_pass = !small_x && !x_gs;
+    if (amax_pass) {
+        NVFP4_TRY(launch_zero_u32(amax, 1, stream));
+        NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
     }
+    const SmallQuant sq = {x, x_gs, amax_pass ? amax : nullptr, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
+    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
+                           slot_row, tiles, num_tiles, amax + 1, 1, &sq, stream));
+    NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
     // 3. L1 grouped GEMM with fused SiLU(gate) * up
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
     GemmParams p1 = {};

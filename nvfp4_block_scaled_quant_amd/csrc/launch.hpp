@@ -83,11 +83,15 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
                              const uint32_t* amax_slots, uint8_t* q, uint8_t* sf, float* alpha,
                              hipStream_t s);
 
-// Quantization of a small activation done inside the routing launch by extra
-// work-groups (each reduces the whole amax, then quantizes its share).
+// Quantization of the activation done inside the routing launch by extra
+// work-groups, concurrently with the routing work-group: each takes the global
+// scale from gs_in (static), else from the amax in *amax_in (computed by an
+// earlier launch), else reduces the whole amax itself (small inputs), then
+// quantizes its share of the 16-element blocks.
 struct SmallQuant {
     const uint16_t* x;
-    const float* gs_in;      // static global scale, or null for amax / 2688
+    const float* gs_in;      // static global scale, or null
+    const uint32_t* amax_in; // amax as float bits, or null
     int64_t M, K;
     uint8_t* q;
     int64_t ldq;

@@ -33,15 +33,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t* __restrict__ slot_row, Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles,
     uint32_t* __restrict__ zero_slots, int n_zero, SmallQuant xq) {
     if (blockIdx.x > 0) {
-        // small activation: every quantization work-group reduces the amax of
-        // all of x (a few hundred KB at most, from L2) and then quantizes its
-        // own share of the 16-element blocks
-        // (with a static global scale the amax is not needed)
+        // quantization work-groups: the global scale is static, or comes from
+        // an amax computed before this launch, or (a small activation: a few
+        // hundred KB at most, from L2) every work-group reduces the amax of all
+        // of x itself; then each quantizes its share of the 16-element blocks
         __shared__ uint32_t wmax[kWaves];
         const int tid = threadIdx.x;
         QuantScales qs;
         if (xq.gs_in) {
             qs = scales_from_gs(*xq.gs_in);
+        } else if (xq.amax_in) {
+            qs = make_scales(__uint_as_float(*xq.amax_in));
         } else {
             const int64_t n = xq.M * xq.K;
             const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
@@ -344,7 +346,7 @@ hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, 
     while ((1 << nbits) < E) ++nbits;
     const size_t lds = sizeof(int32_t) * ((size_t)E * (2 + kWaves) + 1);
     const SmallQuant none = {};
-    // work-groups 1.. quantize the small activation, one 16-element block per thread
+    // work-groups 1.. quantize the activation, one 16-element block per thread
     const int64_t qgroups = xq ? (xq->M * (xq->K / 16) + kRouteThreads - 1) / kRouteThreads : 0;
     route_kernel<<<(unsigned)(1 + qgroups), kRouteThreads, lds, s>>>(ids, S, E, BM, nbits, counts, offsets, sorted_slot,
                                                         slot_row, tiles, num_tiles, zero_slots, n_zero,
