@@ -310,7 +310,7 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
  * ------------------------------------------------------------------------ */
 typedef struct nvfp4_moe_options {
     int32_t w13_alpha_per_half;
-    int32_t reserved;               /* 0 */
+    int32_t reserved;               /* must be 0 (else NVFP4_EINVAL) */
     const float* x_global_scale;
 } nvfp4_moe_options;
 

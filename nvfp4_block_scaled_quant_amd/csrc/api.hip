@@ -291,6 +291,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     const int per_half = options ? options->w13_alpha_per_half : 0;
     const float* x_gs = options ? options->x_global_scale : nullptr;
     if (per_half != 0 && per_half != 1) return NVFP4_EINVAL;
+    if (options && options->reserved != 0) return NVFP4_EINVAL;
     if (x_gs && !aligned(x_gs, 4)) return NVFP4_EINVAL;
     if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
     if (!w13 || !w13_sf || !w13_alpha || !w2 || !w2_sf || !w2_alpha) return NVFP4_EINVAL;

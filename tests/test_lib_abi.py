@@ -156,6 +156,7 @@ def test_moe_forward_ex_option_errors(nv):
     assert call(nv.MoeOptions(2, 0, None)) == 1              # per_half must be 0 or 1
     assert call(nv.MoeOptions(-1, 0, None)) == 1
     assert call(nv.MoeOptions(0, 0, A16 + 2)) == 1           # misaligned static scale
+    assert call(nv.MoeOptions(0, 7, None)) == 1               # reserved must be 0
     assert call(nv.MoeOptions(1, 0, A16)) == 3               # valid options, then the workspace
     assert call(nv.MoeOptions(1, 0, A16), T=0) == 3
 
