@@ -172,6 +172,21 @@ def test_repeat_is_bit_identical(nv):
     assert all((y == g["ys"][0]).all() for y in g["ys"])
 
 
+@pytest.mark.parametrize("static", [False, True])
+def test_repeat_is_bit_identical_large_x(nv, static):
+    # x above 128K elements: amax pass, then the quantization in the routing
+    # launch beside the routing work-group; repeated calls agree bit for bit
+    cfg = W.small_layer("repx", T=300, H=512, I=256, E=8, topk=4, seed=13)
+    assert cfg.T * cfg.H > 1 << 17
+    L = make_layer(cfg)
+    if static:
+        from oracle.formats import bf16_to_f32
+        from oracle.quantize import global_scale
+        L["x_gs"] = np.float32(global_scale(np.float32(np.abs(bf16_to_f32(L["x"])).max())) * np.float32(0.5))
+    g = run_gpu_layer(nv, L, repeat=3)
+    assert all((y == g["ys"][0]).all() for y in g["ys"])
+
+
 # ---- degenerate and boundary cases -------------------------------------------
 
 def test_empty_batch(nv):
