@@ -99,7 +99,7 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t, dtype, name, dim=None):
+def _need(t, dtype, name, dim=None, device=None):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a CUDA (HIP) tensor")
     if t.dtype != dtype:
@@ -108,6 +108,35 @@ def _need(t, dtype, name, dim=None):
         raise ValueError(f"{name} must be contiguous")
     if dim is not None and t.dim() != dim:
         raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _out(t, shape, dtype, device, name):
+    """A caller-given output tensor (checked: the kernels write exactly
+    `shape`), or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, dtype, name, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _workspace(t, nbytes, device):
+    """A caller-given workspace (any dtype, its size in bytes is passed on and
+    checked by the library), or a new uint8 one of nbytes."""
+    if t is None:
+        return torch.empty((nbytes,), dtype=torch.uint8, device=device)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA (HIP) tensor")
+    if t.device != device:
+        raise ValueError(f"workspace is on {t.device}, the other operands on {device}")
+    return t
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def version():
@@ -125,13 +154,12 @@ def quantize(x, q=None, sf=None, gs=None, workspace=None):
     _need(x, torch.bfloat16, "x", 2)
     M, K = x.shape
     dev = x.device
-    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
-    sf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
-    gs = torch.empty((1,), dtype=torch.float32, device=dev) if gs is None else gs
-    nws = _lib.nvfp4_quantize_workspace(M, K)
-    ws = torch.empty((nws,), dtype=torch.uint8, device=dev) if workspace is None else workspace
+    q = _out(q, (M, K // 2), torch.uint8, dev, "q")
+    sf = _out(sf, (M, K // 16), torch.uint8, dev, "sf")
+    gs = _out(gs, (1,), torch.float32, dev, "gs")
+    ws = _workspace(workspace, _lib.nvfp4_quantize_workspace(M, K), dev)
     _check(_lib.nvfp4_quantize(_ptr(x), M, K, _ptr(q), _ptr(sf), _ptr(gs), _ptr(ws),
-                               ws.numel(), _stream()), "nvfp4_quantize")
+                               _nbytes(ws), _stream()), "nvfp4_quantize")
     return q, sf, gs
 
 
@@ -139,11 +167,13 @@ def quantize_static(x, gs, q=None, sf=None):
     """NVFP4-quantize a bf16 (M, K) activation with the given global scale gs
     (float32 (1,) on the device). Returns (q uint8 (M, K/2), sf uint8 (M, K/16))."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(gs, torch.float32, "gs", 1)
     M, K = x.shape
     dev = x.device
-    q = torch.empty((M, K // 2), dtype=torch.uint8, device=dev) if q is None else q
-    sf = torch.empty((M, K // 16), dtype=torch.uint8, device=dev) if sf is None else sf
+    _need(gs, torch.float32, "gs", 1, dev)
+    if gs.numel() < 1:
+        raise ValueError("gs must hold one float32")
+    q = _out(q, (M, K // 2), torch.uint8, dev, "q")
+    sf = _out(sf, (M, K // 16), torch.uint8, dev, "sf")
     _check(_lib.nvfp4_quantize_static(_ptr(x), M, K, _ptr(gs), _ptr(q), _ptr(sf), _stream()),
            "nvfp4_quantize_static")
     return q, sf
@@ -162,7 +192,7 @@ def quantize_weights_parts(w, parts):
     nws = _lib.nvfp4_quantize_weights_parts_workspace(E, K, N, parts)
     ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     _check(_lib.nvfp4_quantize_weights_parts(_ptr(w), E, K, N, parts, _ptr(q), _ptr(sf),
-                                             _ptr(alpha), _ptr(ws), ws.numel(), _stream()),
+                                             _ptr(alpha), _ptr(ws), _nbytes(ws), _stream()),
            "nvfp4_quantize_weights_parts")
     return q, sf, alpha
 
@@ -173,12 +203,10 @@ def route_topk(logits, topk, ids=None, weights=None):
     _need(logits, torch.float32, "logits", 2)
     T, E = logits.shape
     dev = logits.device
-    ids = torch.empty((T, topk), dtype=torch.int32, device=dev) if ids is None else ids
-    weights = torch.empty((T, topk), dtype=torch.float32, device=dev) if weights is None else weights
-    _need(ids, torch.int32, "ids", 2)
-    _need(weights, torch.float32, "weights", 2)
-    if ids.shape != (T, topk) or weights.shape != (T, topk):
-        raise ValueError("route_topk: output shapes must be (T, topk)")
+    if topk < 1:
+        raise ValueError("route_topk: topk must be at least 1")
+    ids = _out(ids, (T, topk), torch.int32, dev, "ids")
+    weights = _out(weights, (T, topk), torch.float32, dev, "weights")
     _check(_lib.nvfp4_route_topk(_ptr(logits), T, E, topk, _ptr(ids), _ptr(weights), _stream()),
            "nvfp4_route_topk")
     return ids, weights
@@ -196,7 +224,7 @@ def quantize_weights(w):
     nws = _lib.nvfp4_quantize_weights_workspace(E, K, N)
     ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     _check(_lib.nvfp4_quantize_weights(_ptr(w), E, K, N, _ptr(q), _ptr(sf), _ptr(alpha), _ptr(ws),
-                                       ws.numel(), _stream()), "nvfp4_quantize_weights")
+                                       _nbytes(ws), _stream()), "nvfp4_quantize_weights")
     return q, sf, alpha
 
 
@@ -226,7 +254,7 @@ def prepack_weights(q, sf):
     """Canonical quantized weights q (E, K/2, N), sf (E, K/16, N) -> the packed
     layout that gemm and moe_forward read (see packed_shapes)."""
     _need(q, torch.uint8, "q", 3)
-    _need(sf, torch.uint8, "sf", 3)
+    _need(sf, torch.uint8, "sf", 3, q.device)
     E, Kh, N = q.shape
     K = 2 * Kh
     if sf.shape != (E, K // 16, N):
@@ -243,10 +271,13 @@ def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
     """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times one
     packed weight matrix bq (N/16, K/128, 16, 64) + bsf (N/16, quads, 16, 32)
     (packed_shapes with E dropped) -> bf16 (M, N). K % 128 == 0."""
-    for t, n, d in ((aq, "aq", torch.uint8), (asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
+    _need(aq, torch.uint8, "aq")
+    for t, n, d in ((asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
                     (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
                     (b_alpha, "b_alpha", torch.float32)):
-        _need(t, d, n)
+        _need(t, d, n, None, aq.device)
+    if a_gs.numel() < 1 or b_alpha.numel() < 1:
+        raise ValueError("gemm: a_gs and b_alpha must hold one float32 each")
     if aq.dim() != 2 or bq.dim() != 4:
         raise ValueError("gemm: aq must be (M, K/2) and bq (N/16, K/128, 16, 64)")
     M = aq.shape[0]
@@ -255,7 +286,7 @@ def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
     if (K % 128 or tuple(bq.shape) != (N // 16, K // 128, 16, 64) or asf.shape != (M, K // 16)
             or tuple(bsf.shape) != packed_shapes(1, K, N)[1][1:]):
         raise ValueError("operand shapes do not match")
-    out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device) if out is None else out
+    out = _out(out, (M, N), torch.bfloat16, aq.device, "out")
     _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),
                            M, N, K, _ptr(out), _stream()), "nvfp4_gemm")
     return out
@@ -284,14 +315,17 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     stage_events: None or a StageEvents; returns y (T, H) bf16.
     """
     _need(x, torch.bfloat16, "x", 2)
-    _need(topk_ids, torch.int32, "topk_ids", 2)
-    _need(topk_weights, torch.float32, "topk_weights", 2)
+    dev = x.device
+    _need(topk_ids, torch.int32, "topk_ids", 2, dev)
+    _need(topk_weights, torch.float32, "topk_weights", 2, dev)
     for t, n in ((w13, "w13"), (w13_sf, "w13_sf"), (w2, "w2"), (w2_sf, "w2_sf")):
-        _need(t, torch.uint8, n, 5)
-    _need(w13_alpha, torch.float32, "w13_alpha")
-    _need(w2_alpha, torch.float32, "w2_alpha", 1)
+        _need(t, torch.uint8, n, 5, dev)
+    _need(w13_alpha, torch.float32, "w13_alpha", None, dev)
+    _need(w2_alpha, torch.float32, "w2_alpha", 1, dev)
     if x_gs is not None:
-        _need(x_gs, torch.float32, "x_gs", 1)
+        _need(x_gs, torch.float32, "x_gs", 1, dev)
+        if x_gs.numel() < 1:
+            raise ValueError("x_gs must hold one float32")
     T, H = x.shape
     topk = topk_ids.shape[1]
     E = w13.shape[0]
@@ -305,23 +339,21 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
             or w13_alpha.shape not in ((E,), (E, 2)) or w2_alpha.shape != (E,)
             or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
         raise ValueError("moe_forward: inconsistent shapes")
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if y is None else y
-    nws = moe_workspace_size(T, H, I, E, topk)
-    if workspace is None:
-        workspace = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    y = _out(y, (T, H), torch.bfloat16, dev, "y")
+    workspace = _workspace(workspace, moe_workspace_size(T, H, I, E, topk), dev)
     ev = stage_events.handles if stage_events is not None else None
     per_half = w13_alpha.dim() == 2
     if not per_half and x_gs is None:
         _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
                                       _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
                                       _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
-                                      workspace.numel(), _stream(), ev), "nvfp4_moe_forward")
+                                      _nbytes(workspace), _stream(), ev), "nvfp4_moe_forward")
         return y
     opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None)
     _check(_lib.nvfp4_moe_forward_ex(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
                                      _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
                                      _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
-                                     workspace.numel(), _stream(), ev, ctypes.byref(opts)),
+                                     _nbytes(workspace), _stream(), ev, ctypes.byref(opts)),
            "nvfp4_moe_forward_ex")
     return y
 
