@@ -275,13 +275,12 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&
 
 // Quantize block b of a row-major (rows, K) bf16 matrix (groups = K / 16
 // blocks per row) into rows of pitch ldq (packed) and ldsf (scales).
-__device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ x, int64_t b,
-                                                   int64_t groups, const QuantScales& qs,
-                                                   uint8_t* __restrict__ q, int64_t ldq,
-                                                   uint8_t* __restrict__ sf, int64_t ldsf) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
-    const u32x4 v0 = src[0];
-    const u32x4 v1 = src[1];
+// Block b (row b / groups, group b % groups) of a row-major bf16 matrix whose
+// 16 elements v0, v1 (8 bf16 pairs) are already loaded: quantize and store it.
+__device__ __forceinline__ void quantize_row_block_loaded(u32x4 v0, u32x4 v1, int64_t b,
+                                                          int64_t groups, const QuantScales& qs,
+                                                          uint8_t* __restrict__ q, int64_t ldq,
+                                                          uint8_t* __restrict__ sf, int64_t ldsf) {
     const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     uint32_t packed[2];
     const uint32_t code = quantize_block16(w, qs, packed);
@@ -297,6 +296,14 @@ __device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ 
         for (int64_t j = groups * 8; j < ldq; j += 8) *reinterpret_cast<u32x2*>(q + r * ldq + j) = (u32x2){0u, 0u};
         for (int64_t j = groups; j < ldsf; ++j) sf[r * ldsf + j] = 0;
     }
+}
+
+__device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ x, int64_t b,
+                                                   int64_t groups, const QuantScales& qs,
+                                                   uint8_t* __restrict__ q, int64_t ldq,
+                                                   uint8_t* __restrict__ sf, int64_t ldsf) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
+    quantize_row_block_loaded(src[0], src[1], b, groups, qs, q, ldq, sf, ldsf);
 }
 
 }  // namespace nvfp4

@@ -18,6 +18,8 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+// 16-element blocks per thread and pass of the row quantizer
+constexpr int kRowBlocks = 4;
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
@@ -77,9 +79,23 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const int64_t rows = m_dev ? min((int64_t)(*m_dev), M) : M;
     const int64_t groups = K / 16;
     const int64_t nblocks = rows * groups;
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
-         b += (int64_t)gridDim.x * kThreads)
-        quantize_row_block(x, b, groups, qs, q, ldq, sf, ldsf);
+    const int64_t step = (int64_t)gridDim.x * kThreads;
+    int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // kRowBlocks blocks per thread and pass, all their loads issued before the
+    // first is quantized (one block's two loads alone leave HBM underused)
+    for (; b + (kRowBlocks - 1) * step < nblocks; b += kRowBlocks * step) {
+        u32x4 v[kRowBlocks][2];
+#pragma unroll
+        for (int u = 0; u < kRowBlocks; ++u) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(x + (b + u * step) * 16);
+            v[u][0] = src[0];
+            v[u][1] = src[1];
+        }
+#pragma unroll
+        for (int u = 0; u < kRowBlocks; ++u)
+            quantize_row_block_loaded(v[u][0], v[u][1], b + u * step, groups, qs, q, ldq, sf, ldsf);
+    }
+    for (; b < nblocks; b += step) quantize_row_block(x, b, groups, qs, q, ldq, sf, ldsf);
 }
 
 // Canonical (R, C) byte matrices -> the packed weight layout (launch.hpp),
@@ -202,7 +218,7 @@ hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, u
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
                              const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
                              int64_t ldsf, float* gs_out, hipStream_t s, const float* gs_in) {
-    const int g = grid_for(M * (K / 16), 1 << 20);
+    const int g = grid_for((M * (K / 16) + kRowBlocks - 1) / kRowBlocks, 1 << 20);
     quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, gs_in, q, ldq, sf, ldsf, gs_out);
     return hipGetLastError();
 }
