@@ -259,3 +259,50 @@ def test_tile_row_block_variants(nv):
     L["ids"] = np.repeat(np.arange(4, dtype=np.int32), counts)[np.random.default_rng(27).permutation(T)][:, None]
     g, _, _ = compare_layer(nv, L, "tile row-block variants")
     assert list(g["counts"]) == counts
+
+
+def _exact_gate_up_layer(T, E, I, seed):
+    """A layer whose gate and up values are single exact products on both
+    sides: x has one nonzero per row (column 0, so each gate/up element is
+    x̂[t, 0] · ŵ[0, n]), gs1 = 1 (x amax 2688) and every w13 alpha = 2^-10
+    (w13 amax 2.625), so the float32 accumulation and the alpha scaling are
+    exact and g, u reach the SiLU bit-identical to the oracle's. act must
+    then match bit for bit: this pins the correctly rounded SiLU·up."""
+    from oracle.formats import bf16_from_f64
+    from oracle.quantize import quantize_weight_bf16
+    rng = np.random.default_rng(seed)
+    H = 16
+    xv = np.zeros((T, H))
+    xv[:, 0] = rng.choice([-1.0, 1.0], T) * 2.0 ** rng.uniform(-3, 6, T)
+    xv[0, 0] = 2688.0
+    L = dict(x=bf16_from_f64(xv),
+             ids=(np.arange(T) % E).astype(np.int32)[:, None],
+             wts=np.ones((T, 1), np.float32))
+    w13q = np.zeros((E, H // 2, 2 * I), np.uint8)
+    w13sf = np.zeros((E, H // 16, 2 * I), np.uint8)
+    w2q = np.zeros((E, I // 2, H), np.uint8)
+    w2sf = np.zeros((E, I // 16, H), np.uint8)
+    w13a = np.zeros(E, np.float32)
+    w2a = np.zeros(E, np.float32)
+    for e in range(E):
+        w13 = rng.uniform(-1.0, 1.0, (H, 2 * I)) * 2.625
+        w13[0, 0] = 2.625
+        w13q[e], w13sf[e], w13a[e] = quantize_weight_bf16(bf16_from_f64(w13))
+        w2q[e], w2sf[e], w2a[e] = quantize_weight_bf16(bf16_from_f64(rng.standard_normal((I, H)) * 0.02))
+    assert (w13a == np.float32(2.0 ** -10)).all()
+    L.update(w13q=w13q, w13sf=w13sf, w13a=w13a, w2q=w2q, w2sf=w2sf, w2a=w2a)
+    return L
+
+
+@pytest.mark.parametrize("T,E,I", [(256, 1, 256), (512, 2, 320), (96, 8, 256)])
+def test_silu_up_bit_exact_on_exact_gate_up(nv, T, E, I):
+    # (256, 1): 256-row MFMA tiles; (512, 2): two experts, partial N tile;
+    # (96, 8): 12 slots per expert, the weight-streaming path
+    L = _exact_gate_up_layer(T, E, I, seed=T + E)
+    g, r, _ = compare_layer(nv, L, f"exact gate/up T{T} E{E} I{I}", min_act_exact=1.0)
+    assert g["gs1"] == np.float32(1.0)
+    gu = r["gu"][:, 0, :]
+    gate = gu[:, :I]
+    # the inputs reach the float64 fallback's regions: gates below -87 and
+    # gates so large that silu(g) * u rounds like the plain product g * u
+    assert (gate < -87).any() and (gate > 17).any()
