@@ -81,16 +81,71 @@ __device__ __forceinline__ double exp_f64(double x) {
     return __builtin_ldexp(p, (int)n);
 }
 
-// e^-|g| for |g| <= 87 (the result stays a normal float): the hardware base-2
-// exponential (1 ulp) of t = -|g| log2(e) rounded to float, times
-// 1 + (rest of the product) ln 2, which restores the bits lost in rounding t
-// (|rest| < 2^-17, so the linear term is exact to far below an ulp).
-__device__ __forceinline__ float exp_neg_abs(float g) {
-    const float a = -fabsf(g);
-    const float t = a * 1.44269502f;                                           // log2(e), head
-    const float rest = __builtin_fmaf(a, 1.44269502f, -t) + a * 1.925963e-8f; // tail of a log2(e)
+// e^x, accurate for x <= 87 (the result stays a normal float: e^87 < 2^126):
+// the hardware base-2 exponential (1 ulp) of t = x log2(e) rounded to float,
+// times 1 + r, r = (x log2(e) - t) ln 2. The residual x log2(e) - t is the
+// exact rounding error of the product (one fma) plus x times the tail of
+// log2(e); |r| < 2^-17, so its own rounding is far below an ulp of the result.
+// Larger x give +inf (or 2^128-range garbage that the callers reject).
+__device__ __forceinline__ float exp_split(float x) {
+    const float t = x * 1.44269502f;                                           // log2(e), head
+    const float r = __builtin_fmaf(__builtin_fmaf(x, 1.44269502f, -t), 0.693147182f,
+                                   x * (1.925963e-8f * 0.693147182f));         // tail of log2(e), times ln 2
     const float p = __builtin_amdgcn_exp2f(t);
-    return __builtin_fmaf(p, rest * 0.693147182f, p);
+    return __builtin_fmaf(p, r, p);
+}
+
+// act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
+// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
+// A float32 evaluation (relative error a few ulps) decides the rounding when
+// it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
+// e^g leaves the float32 normal range, the product is recomputed in float64.
+// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
+// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
+// would round the wrong way.)
+// Whether the float32 value v of silu(g) * u (below) decides the correctly
+// rounded bf16 result: g >= -87, v normal, and the 16 bits of v below bf16
+// precision more than 32 from the rounding midpoint 0x8000, i.e.
+// (low - 0x8000 + 32) mod 2^16 > 64.
+__device__ __forceinline__ bool silu_f32_decides(float g, float v) {
+    const uint32_t m = (__float_as_uint(v) + 0x8020u) & 0xFFFFu;
+    return (g >= -87.0f) & __builtin_isnormal(v) & (m > 64u);
+}
+
+// float32 evaluation of silu(g) * u.
+__device__ __forceinline__ float silu_mul_value(float g, float u) {
+    // silu(g) = g / (1 + e^-g) for every g >= -87: e^-g <= e^87 is finite and
+    // the reciprocal of 1 + e^-g (>= 1.6e-38) is still a normal float, so one
+    // formula serves both signs. Error: the exponential about 2 ulps, the sum
+    // half an ulp, the hardware reciprocal 1 ulp, the two products half an ulp
+    // each: under 5 ulps, well inside the 32-ulp margin of silu_f32_decides.
+    // Below g = -87 (and for non-finite g) v is wrong, zero or NaN, and those
+    // gates always go to float64.
+    const float e = exp_split(-g);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// The same value and whether it decides the correctly rounded bf16 result.
+__device__ __forceinline__ float silu_mul_f32(float g, float u, bool& ok) {
+    const float v = silu_mul_value(g, u);
+    ok = silu_f32_decides(g, v);
+    return v;
+}
+
+// The lanes of the wave whose (g, v) silu_f32_decides rejects, as a mask:
+// one ballot per condition, so each is the compare's own lane mask.
+__device__ __forceinline__ uint64_t silu_f32_redo_lanes(float g, float v) {
+    const uint32_t m = (__float_as_uint(v) + 0x8020u) & 0xFFFFu;
+    // v not normal: |v| below the smallest normal (zero, subnormal; NaN
+    // compares false) or not below infinity
+    const float av = fabsf(v);
+    return __builtin_amdgcn_ballot_w64(!(g >= -87.0f)) | __builtin_amdgcn_ballot_w64(!(av >= 0x1p-126f)) |
+           __builtin_amdgcn_ballot_w64(!(av < __builtin_inff())) | __builtin_amdgcn_ballot_w64(m <= 64u);
+}
+
+__device__ __forceinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
+    const double gd = g, ud = u;
+    return f64_to_bf16_rne((gd / (1.0 + exp_f64(-gd))) * ud);
 }
 
 // act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
@@ -102,23 +157,25 @@ __device__ __forceinline__ float exp_neg_abs(float g) {
 // about 1 in 256 of those products is a bf16 midpoint, which float32 alone
 // would round the wrong way.)
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
-    // silu(g) = g / (1 + e^-g) = g e^g / (1 + e^g); one exponential of -|g|
-    // serves both signs. Error: the exponential about 2 ulps, the hardware
-    // reciprocal 1 ulp, the sum and the three products half an ulp each:
-    // under 6 ulps, well inside the 32-ulp margin below. Computed without
-    // branches (g clamped to -87 for the exponential); the float64 path is
-    // the only branch.
-    const float e = exp_neg_abs(fmaxf(g, -87.0f));
-    const float num = (g >= 0.0f) ? g : g * e;
-    const float v = num * __builtin_amdgcn_rcpf(1.0f + e) * u;
-    const uint32_t b = __float_as_uint(v);
-    const uint32_t low = b & 0xFFFFu;
-    const uint32_t dist = low > 0x8000u ? low - 0x8000u : 0x8000u - low;
-    const uint32_t ex = b & 0x7F800000u;
-    const bool ok = (g >= -87.0f) & (ex != 0u) & (ex != 0x7F800000u) & (dist > 32u);
+    bool ok;
+    const float v = silu_mul_f32(g, u, ok);
     if (__builtin_expect(ok, 1)) return f32_to_bf16_rne(v);
-    const double gd = g, ud = u;
-    return f64_to_bf16_rne((gd / (1.0 + exp_f64(-gd))) * ud);
+    return silu_mul_bf16_f64(g, u);
+}
+
+// Two of them as one packed pair (first in the low half): the float32 results
+// are rounded together by the hardware pair conversion (nearest-even, the same
+// rounding for normal values), and each element that float32 cannot decide is
+// replaced by its float64 result (a branch per element, taken only by waves
+// with such an element).
+__device__ __forceinline__ uint32_t silu_mul_bf16x2(float g0, float u0, float g1, float u1) {
+    bool ok0, ok1;
+    const float v0 = silu_mul_f32(g0, u0, ok0);
+    const float v1 = silu_mul_f32(g1, u1, ok1);
+    uint32_t r = pack_bf16x2_rne(v0, v1);
+    if (__builtin_expect(!ok0, 0)) r = (r & 0xFFFF0000u) | silu_mul_bf16_f64(g0, u0);
+    if (__builtin_expect(!ok1, 0)) r = (r & 0xFFFFu) | (silu_mul_bf16_f64(g1, u1) << 16);
+    return r;
 }
 
 // ---------------------------------------------------------------------------

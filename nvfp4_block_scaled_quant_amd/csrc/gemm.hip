@@ -221,28 +221,43 @@ void gemm_kernel(GemmParams p) {
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
         u32x4 fa[MI][2], fb[4][2];
-        uint32_t sa[MI], sb[4];
+        uint32_t sa[MI];
+        u32x2 sb[4];      // B scale pairs 2h, 2h + 1: bytes 0-1 of each dword
+        // Fragment rows are wm * 32 MI + 32 i + l32 (A) and wn * 128 + 32 j + l32
+        // (B): the 32 i / 32 j parts are multiples of 16, so the swizzle (bits
+        // 2-3 of the row) depends on the lane alone. Six per-lane offsets
+        // within a stage are formed once; per step each gets the stage base
+        // added once, and the fragments' row offsets are constants (the LDS
+        // reads' immediate offsets), instead of a full address per read.
+        const int sw = (l32 >> 2) & 3;
+        const uint32_t a_row = (uint32_t)(wm * (32 * MI) + l32), b_row = (uint32_t)(wn * 128 + l32);
+        const uint32_t off_a0 = a_row * KB + 16 * ((2 * h) ^ sw);
+        const uint32_t off_a1 = a_row * KB + 16 * ((2 * h + 1) ^ sw);
+        const uint32_t off_b0 = A_BYTES + b_row * KB + 16 * ((2 * h) ^ sw);
+        const uint32_t off_b1 = A_BYTES + b_row * KB + 16 * ((2 * h + 1) ^ sw);
+        const uint32_t off_asf = A_BYTES + B_BYTES + a_row * 8 + 4 * h;
+        const uint32_t off_bsf = A_BYTES + B_BYTES + ASF_BYTES + b_row * 16 + 8 * h;
         auto read_frags = [&](int ks) {
             const uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-            const uint8_t* sA = base;
-            const uint8_t* sB = base + A_BYTES;
-            const uint8_t* sAsf = base + A_BYTES + B_BYTES;
-            const uint8_t* sBsf = sAsf + ASF_BYTES;
+            const uint8_t* pa0 = base + off_a0;
+            const uint8_t* pa1 = base + off_a1;
+            const uint8_t* pb0 = base + off_b0;
+            const uint8_t* pb1 = base + off_b1;
+            const uint8_t* pas = base + off_asf;
+            const uint8_t* pbs = base + off_bsf;
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
-                const int row = wm * (32 * MI) + 32 * i + l32;
-                fa[i][0] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h));
-                fa[i][1] = *reinterpret_cast<const u32x4*>(sA + row * KB + 16 * swz(row, 2 * h + 1));
-                sa[i] = *reinterpret_cast<const uint32_t*>(sAsf + row * 8 + 4 * h);
+                fa[i][0] = *reinterpret_cast<const u32x4*>(pa0 + i * 32 * KB);
+                fa[i][1] = *reinterpret_cast<const u32x4*>(pa1 + i * 32 * KB);
+                sa[i] = *reinterpret_cast<const uint32_t*>(pas + i * 32 * 8);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int vc = wn * 128 + 32 * j + l32;
-                fb[j][0] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h));
-                fb[j][1] = *reinterpret_cast<const u32x4*>(sB + vc * KB + 16 * swz(vc, 2 * h + 1));
-                // pairs 2h and 2h + 1, each in the low half of its dword
-                const u32x2 d = *reinterpret_cast<const u32x2*>(sBsf + vc * 16 + 8 * h);
-                sb[j] = d[0] | (d[1] << 16);
+                fb[j][0] = *reinterpret_cast<const u32x4*>(pb0 + j * 32 * KB);
+                fb[j][1] = *reinterpret_cast<const u32x4*>(pb1 + j * 32 * KB);
+                // pairs 2h and 2h + 1, each in the low half of its dword (the
+                // dequant picks the byte from either, no joining needed)
+                sb[j] = *reinterpret_cast<const u32x2*>(pbs + j * 32 * 16);
             }
         };
         // operands of substep s in registers s & 1
@@ -253,7 +268,7 @@ void gemm_kernel(GemmParams p) {
                 xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu));
+                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j][s >> 2] >> (8 * ((s >> 1) & 1))) & 0xFFu));
         };
 
         // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
@@ -348,6 +363,8 @@ void gemm_kernel(GemmParams p) {
             static_assert(64 * MI * GU_LD * 4 <= LDS_BYTES, "gate/up staging fits in LDS");
             uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [64 MI][GU_LD] g | u << 16
             uint32_t amax_bits = 0;
+            typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+            u16x2_t amax_pair = {0, 0};
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -370,18 +387,66 @@ void gemm_kernel(GemmParams p) {
                     uint32_t* dst = reinterpret_cast<uint32_t*>(p.out_bf16 + (int64_t)(row_start + r0) * p.I + col);
                     const int64_t dstep = 2 * p.I;                // 4 rows, in 4-byte units
                     const int rows = min(row_count, 64 * MI);
-                    // unrolled: the LDS reads of four rows are in flight together
-                    // (one wave per SIMD has nothing else to hide their latency)
-#pragma unroll 4
-                    for (int r = r0; r < rows; r += NT / 64, dst += dstep) {
+                    // Four rows per pass: their eight float32 SiLUs form one
+                    // branch-free block of independent chains (one wave per SIMD
+                    // has nothing else to hide the exp / rcp latencies), and the
+                    // elements float32 cannot decide are redone in float64 after
+                    // it, behind one branch that is rarely taken.
+                    constexpr int RS = NT / 64;                   // row step of a thread
+                    int r = r0;
+                    for (; r + 3 * RS < rows; r += 4 * RS, dst += 4 * dstep) {
+                        float g[8], u[8], v[8];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const u32x2 w = *reinterpret_cast<const u32x2*>(gu + (r + k * RS) * GU_LD + 2 * cp);
+                            g[2 * k] = bf16_to_f32(w[0] & 0xFFFFu);
+                            u[2 * k] = bf16_to_f32(w[0] >> 16);
+                            g[2 * k + 1] = bf16_to_f32(w[1] & 0xFFFFu);
+                            u[2 * k + 1] = bf16_to_f32(w[1] >> 16);
+                        }
+                        // lanes with an element float32 cannot decide, as a
+                        // wave mask (scalar ORs of the compare masks)
+                        uint64_t redo = 0;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            v[i] = silu_mul_value(g[i], u[i]);
+                            redo |= silu_f32_redo_lanes(g[i], v[i]);
+                        }
+                        uint32_t a[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) a[k] = pack_bf16x2_rne(v[2 * k], v[2 * k + 1]);
+                        if (__builtin_expect(redo != 0, 0)) {
+                            // the test is repeated here on values the compiler
+                            // cannot see through, so the block above keeps only
+                            // the combined flag (not eight per-element ones)
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                asm volatile("" : "+v"(g[i]), "+v"(v[i]));
+                                if (!silu_f32_decides(g[i], v[i])) {
+                                    const uint32_t b = silu_mul_bf16_f64(g[i], u[i]);
+                                    a[i >> 1] = (i & 1) ? ((a[i >> 1] & 0xFFFFu) | (b << 16))
+                                                        : ((a[i >> 1] & 0xFFFF0000u) | b);
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            dst[k * dstep] = a[k];
+                            // |act| bit patterns of both halves, maximum per half
+                            amax_pair = __builtin_elementwise_max(amax_pair,
+                                                                  __builtin_bit_cast(u16x2_t, a[k] & 0x7FFF7FFFu));
+                        }
+                    }
+                    for (; r < rows; r += RS, dst += dstep) {
                         const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * GU_LD + 2 * cp);
-                        const uint32_t a0 = silu_mul_bf16(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16));
-                        const uint32_t a1 = silu_mul_bf16(bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
-                        *dst = a0 | (a1 << 16);
-                        amax_bits = max(amax_bits, max(a0 & 0x7FFFu, a1 & 0x7FFFu));
+                        const uint32_t a = silu_mul_bf16x2(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16),
+                                                           bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
+                        *dst = a;
+                        amax_pair = __builtin_elementwise_max(amax_pair, __builtin_bit_cast(u16x2_t, a & 0x7FFF7FFFu));
                     }
                 }
             }
+            amax_bits = max((uint32_t)amax_pair[0], (uint32_t)amax_pair[1]);
             amax_bits = wave_max_u32(amax_bits);
             if (lane == 0) red[wave] = amax_bits;
             __syncthreads();
