@@ -262,13 +262,22 @@ void gemm_kernel(GemmParams p) {
         };
         // operands of substep s in registers s & 1
         half8_t ha[2][MI], hb[2][4];
+        // scale pairs of the current group of two substeps (one scale group):
+        // formed on even substeps, reused on the odd ones (also across the
+        // step boundary: substep 0 is dequantized at the end of the previous
+        // step)
+        half2_t spa[MI], spb[4];
         auto deq = [&](int s, half8_t (&xa)[MI], half8_t (&xb)[4]) {
+            if ((s & 1) == 0) {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                xa[i] = dequant8(fa[i][s >> 2][s & 3], scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu));
+                for (int i = 0; i < MI; ++i) spa[i] = scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xb[j] = dequant8(fb[j][s >> 2][s & 3], scale_pair((sb[j][s >> 2] >> (8 * ((s >> 1) & 1))) & 0xFFu));
+                for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j][s >> 2] >> (8 * ((s >> 1) & 1))) & 0xFFu);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i) xa[i] = dequant8(fa[i][s >> 2][s & 3], spa[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xb[j] = dequant8(fb[j][s >> 2][s & 3], spb[j]);
         };
 
         // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
