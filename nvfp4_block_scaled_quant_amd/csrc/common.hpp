@@ -86,7 +86,8 @@ __device__ __forceinline__ double exp_f64(double x) {
 // times 1 + r, r = (x log2(e) - t) ln 2. The residual x log2(e) - t is the
 // exact rounding error of the product (one fma) plus x times the tail of
 // log2(e); |r| < 2^-17, so its own rounding is far below an ulp of the result.
-// Larger x give +inf (or 2^128-range garbage that the callers reject).
+// Larger x give values at the top of the float range or +inf (beyond about
+// 88.7); the callers send those gates to float64.
 __device__ __forceinline__ float exp_split(float x) {
     const float t = x * 1.44269502f;                                           // log2(e), head
     const float r = __builtin_fmaf(__builtin_fmaf(x, 1.44269502f, -t), 0.693147182f,
@@ -95,14 +96,6 @@ __device__ __forceinline__ float exp_split(float x) {
     return __builtin_fmaf(p, r, p);
 }
 
-// act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
-// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
-// A float32 evaluation (relative error a few ulps) decides the rounding when
-// it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
-// e^g leaves the float32 normal range, the product is recomputed in float64.
-// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
-// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
-// would round the wrong way.)
 // Whether the float32 value v of silu(g) * u (below) decides the correctly
 // rounded bf16 result: g >= -87, v normal, and the 16 bits of v below bf16
 // precision more than 32 from the rounding midpoint 0x8000, i.e.
