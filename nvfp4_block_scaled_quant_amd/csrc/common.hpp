@@ -138,19 +138,29 @@ __device__ __forceinline__ uint64_t silu_f32_redo_lanes(float g, float v) {
            __builtin_amdgcn_ballot_w64(!(av < __builtin_inff())) | __builtin_amdgcn_ballot_w64(m <= 32u);
 }
 
+// The float64 evaluation. Where 1 + e^-g rounds to 1 (g above about 36.7)
+// the float64 value is the plain product g * u (16 significant bits at most,
+// exact), while the exact value is smaller in magnitude by a factor within
+// 2^-53 of 1: a product that is a bf16 rounding midpoint must then round
+// toward zero, so the value is first moved one float64 step toward zero (no
+// other rounding boundary lies that close to a 16-bit product).
 __device__ __forceinline__ uint32_t silu_mul_bf16_f64(float g, float u) {
     const double gd = g, ud = u;
-    return f64_to_bf16_rne((gd / (1.0 + exp_f64(-gd))) * ud);
+    const double den = 1.0 + exp_f64(-gd);
+    double v = (gd / den) * ud;
+    if (den == 1.0 && v != 0.0 && __builtin_isfinite(v))
+        v = __longlong_as_double(__double_as_longlong(v) - 1);
+    return f64_to_bf16_rne(v);
 }
 
 // act = bf16(silu(g) * u) for bf16-valued g, u (the L1 epilogue), with
-// silu(z) = z / (1 + e^-z), correctly rounded from the float64 value.
+// silu(z) = z / (1 + e^-z), correctly rounded from the exact value.
 // A float32 evaluation (relative error a few ulps) decides the rounding when
 // it is far from a bf16 rounding midpoint; otherwise, and for g < -87 where
-// e^g leaves the float32 normal range, the product is recomputed in float64.
-// (Large gates make silu(g) * u the exact product g * u up to a tiny factor;
-// about 1 in 256 of those products is a bf16 midpoint, which float32 alone
-// would round the wrong way.)
+// e^g leaves the float32 normal range, the product is recomputed in float64
+// (above). (Large gates make silu(g) * u the exact product g * u up to a tiny
+// factor; about 1 in 256 of those products is a bf16 midpoint, which float32
+// alone would round the wrong way.)
 __device__ __forceinline__ uint32_t silu_mul_bf16(float g, float u) {
     bool ok;
     const float v = silu_mul_f32(g, u, ok);

@@ -232,7 +232,13 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
         for n in range(I):
             g, u = gu[n], gu[I + n]
             sil = g / (1.0 + math.exp(-g)) if g > -700.0 else -0.0 * g
-            prod = Fraction(sil) * Fraction(u)
+            if g > 0 and 1.0 + math.exp(-g) == 1.0:
+                # e^-g below 2^-53: the exact value g*u / (1 + e^-g) lies
+                # strictly between g*u*(1 - 2^-52) and g*u, and no bf16
+                # rounding boundary other than g*u itself lies there
+                prod = Fraction(g) * Fraction(u) * (1 - Fraction(1, 1 << 60))
+            else:
+                prod = Fraction(sil) * Fraction(u)
             neg_zero = (math.copysign(1.0, sil) * math.copysign(1.0, u)) < 0
             bits.append(bf16_bits(bf16(prod, negative_zero=neg_zero)))
         act[(t, j)] = bits

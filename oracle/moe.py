@@ -42,6 +42,29 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
+def silu_mul_bf16(g_bits, u_bits):
+    """act = bf16(silu(g) * u) for bf16 inputs g, u (R2), rounded to nearest
+    even from the exact value.
+
+    The float64 value silu(g) * u decides the rounding, with one exception:
+    where 1 + exp(-g) rounds to 1 in float64 (g above about 36.7) it is the
+    plain product g * u (at most 16 significant bits, exact), while the exact
+    value g * u / (1 + e^-g) is smaller in magnitude by a factor within 2^-53
+    of 1. If that product is a bf16 rounding midpoint the exact value lies just
+    inside it, so it must round toward zero; elsewhere the tiny factor cannot
+    move the result across a rounding boundary. The float64 value is therefore
+    moved one float64 step toward zero in that case before the rounding.
+    """
+    g = bf16_to_f32(g_bits).astype(np.float64)
+    u = bf16_to_f32(u_bits).astype(np.float64)
+    with np.errstate(over="ignore"):
+        den = 1.0 + np.exp(-g)
+    v = g / den * u
+    exact_product = (den == 1.0) & (v != 0) & np.isfinite(v)
+    v = np.where(exact_product, np.nextafter(v, 0.0), v)
+    return bf16_from_f64(v)
+
+
 def slots_by_expert(topk_ids, num_experts):
     """For each expert, the (token, choice) pairs routed to it, in (t, j) order."""
     ids = np.asarray(topk_ids)
@@ -62,9 +85,7 @@ def _l1_expert(task):
     ag, au = (alpha, alpha) if np.ndim(alpha) == 0 else (alpha[0], alpha[1])
     gu_f64 = np.concatenate([ag * ab[:, :I], au * ab[:, I:]], axis=1)
     gu = bf16_from_f64(gu_f64)                                       # R1
-    g = bf16_to_f32(gu[:, :I]).astype(np.float64)
-    u = bf16_to_f32(gu[:, I:]).astype(np.float64)
-    return bf16_from_f64(silu(g) * u), (gu_f64 if keep else None)    # R2
+    return silu_mul_bf16(gu[:, :I], gu[:, I:]), (gu_f64 if keep else None)   # R2
 
 
 def _l2_expert(task):
@@ -103,7 +124,6 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     ids = np.asarray(topk_ids).astype(np.int64)
-    wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
     T, H = x_bits.shape
     k = ids.shape[1] if ids.ndim == 2 else 0
     E = w13q.shape[0]
@@ -144,15 +164,7 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
         gs2 = np.float32(0.0)
 
     # stage 5: L2 and the weighted combine, float64 until the final rounding
-    y = np.zeros((T, H), dtype=np.float64)
-    contrib = np.zeros((T, k, H), dtype=np.float64)
-    tasks = [(aq[t_idx, j_idx], asf[t_idx, j_idx], w2q[e], w2sf[e],
-              np.float64(gs2) * np.float64(np.float32(w2_alpha[e])), wts[t_idx, j_idx])
-             for e, (t_idx, j_idx) in enumerate(groups) if t_idx.size]
-    for (t_idx, j_idx), rows in zip(placed, _map(_l2_expert, tasks, pool)):
-        contrib[t_idx, j_idx] = rows
-    for j in range(k):                                               # j order
-        y += contrib[:, j, :]
+    y, contrib = l2_combine(aq, asf, gs2, ids, topk_weights, w2q, w2sf, w2_alpha, pool=pool)
     out = {"y": y, "y_bits": bf16_from_f64(y), "gs1": gs1, "gs2": np.float32(gs2)}
     if keep:
         out.update(xq=xq, xsf=xsf, gu=gu_keep, act_bits=act_bits, aq=aq, asf=asf,
@@ -160,10 +172,38 @@ def moe_forward(x_bits, topk_ids, topk_weights, w13q, w13sf, w13_alpha,
     return out
 
 
+def l2_combine(aq, asf, gs2, topk_ids, topk_weights, w2q, w2sf, w2_alpha, pool=None):
+    """Stage 5 on given requantized activations: the L2 GEMM of each valid
+    slot's row against w2[e] with alpha = gs2 * w2_alpha[e], then y[t] = sum
+    over j, in j order, of topk_weights[t, j] times that row (float64, left
+    unrounded). aq (T, k, I/2) and asf (T, k, I/16) are indexed by (token,
+    choice); rows of skipped slots are not read.
+
+    Returns (y (T, H) float64, contrib (T, k, H) float64 weighted L2 rows).
+    """
+    ids = np.asarray(topk_ids).astype(np.int64)
+    wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
+    T, k = ids.shape
+    E = w2q.shape[0]
+    H = w2q.shape[2]
+    groups = slots_by_expert(ids, E)
+    placed = [(t_idx, j_idx) for t_idx, j_idx in groups if t_idx.size]
+    contrib = np.zeros((T, k, H), dtype=np.float64)
+    tasks = [(aq[t_idx, j_idx], asf[t_idx, j_idx], w2q[e], w2sf[e],
+              np.float64(np.float32(gs2)) * np.float64(np.float32(w2_alpha[e])), wts[t_idx, j_idx])
+             for e, (t_idx, j_idx) in enumerate(groups) if t_idx.size]
+    for (t_idx, j_idx), rows in zip(placed, _map(_l2_expert, tasks, pool)):
+        contrib[t_idx, j_idx] = rows
+    y = np.zeros((T, H), dtype=np.float64)
+    for j in range(k):                                               # j order
+        y += contrib[:, j, :]
+    return y, contrib
+
+
 def quantize_act_rows(act_bits):
     """Stage-4 quantization on its own: rows of bf16 activations."""
     return quantize_bf16(act_bits)
 
 
-__all__ = ["moe_forward", "silu", "slots_by_expert", "quantize_act_rows",
-           "quantize_f32"]
+__all__ = ["moe_forward", "silu", "silu_mul_bf16", "slots_by_expert", "l2_combine",
+           "quantize_act_rows", "quantize_f32"]
