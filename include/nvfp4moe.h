@@ -307,11 +307,22 @@ int nvfp4_moe_forward(const uint16_t* x, const int32_t* topk_ids, const float* t
  *                       float32 (4-byte aligned) used as gs1 for stage 1, as
  *                       in nvfp4_quantize_static (no amax pass; blocks beyond
  *                       6 * 448 * gs1 saturate). gs2 stays dynamic.
+ *   gate_up_tap         NULL (production), or a device buffer of
+ *                       T * topk * 2I bf16 values (4-byte aligned) that
+ *                       receives stage 3's rounded output: row r (sorted
+ *                       order, as the act rows in the workspace; rows beyond
+ *                       the valid slots are not written) holds the gate
+ *                       values in columns [0, I) and the up values in
+ *                       [I, 2I), exactly the bf16 values the SiLU consumes.
+ *                       A debugging and test tap (the pages' lesson: compare
+ *                       each stage on identical inputs); it adds stores and
+ *                       changes no other output.
  * ------------------------------------------------------------------------ */
 typedef struct nvfp4_moe_options {
     int32_t w13_alpha_per_half;
     int32_t reserved;               /* must be 0 (else NVFP4_EINVAL) */
     const float* x_global_scale;
+    uint16_t* gate_up_tap;
 } nvfp4_moe_options;
 
 int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,

@@ -62,7 +62,7 @@ _SIGS = {
 class MoeOptions(ctypes.Structure):
     """struct nvfp4_moe_options."""
     _fields_ = [("w13_alpha_per_half", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("x_global_scale", ctypes.c_void_p)]
+                ("x_global_scale", ctypes.c_void_p), ("gate_up_tap", ctypes.c_void_p)]
 
 
 for _name, (_args, _res) in _SIGS.items():
@@ -306,12 +306,14 @@ def moe_workspace_layout(T, H, I, E, topk):
 
 
 def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
-                y=None, workspace=None, stage_events=None, x_gs=None):
+                y=None, workspace=None, stage_events=None, x_gs=None, gate_up_tap=None):
     """The five-stage NVFP4 expert layer. Weights in the packed layout
     (prepack_weights of the canonical (E, H/2, 2I) and (E, I/2, H) tensors).
 
     w13_alpha: (E,) one weight global scale per expert, or (E, 2) per half
     (gate, up). x_gs: None (dynamic gs1) or a float32 (1,) static gs1.
+    gate_up_tap: None, or a bf16 (T * topk, 2I) tensor that receives the
+    rounded L1 output (sorted rows, gate | up), for stage-by-stage checks.
     stage_events: None or a StageEvents; returns y (T, H) bf16.
     """
     _need(x, torch.bfloat16, "x", 2)
@@ -340,16 +342,19 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
             or topk_ids.shape != (T, topk) or topk_weights.shape != (T, topk)):
         raise ValueError("moe_forward: inconsistent shapes")
     y = _out(y, (T, H), torch.bfloat16, dev, "y")
+    if gate_up_tap is not None:
+        _out(gate_up_tap, (T * topk, 2 * I), torch.bfloat16, dev, "gate_up_tap")
     workspace = _workspace(workspace, moe_workspace_size(T, H, I, E, topk), dev)
     ev = stage_events.handles if stage_events is not None else None
     per_half = w13_alpha.dim() == 2
-    if not per_half and x_gs is None:
+    if not per_half and x_gs is None and gate_up_tap is None:
         _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
                                       _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
                                       _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
                                       _nbytes(workspace), _stream(), ev), "nvfp4_moe_forward")
         return y
-    opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None)
+    opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None,
+                      gate_up_tap.data_ptr() if gate_up_tap is not None else None)
     _check(_lib.nvfp4_moe_forward_ex(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
                                      _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
                                      _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),

@@ -57,8 +57,14 @@ int64_t moe_max_tiles(int64_t S, int64_t E, int64_t BM) {
 }
 
 // Small batches (at most 16 slots per expert on average) stream the weights
-// with 16-row tiles; larger ones use the 256 x 256 MFMA tiles.
-bool moe_use_skinny(int64_t S, int64_t E) { return S <= (int64_t)kSkinnyBM * E; }
+// with 16-row tiles; larger ones use the 256 x 256 MFMA tiles. The streaming
+// kernel stages its A rows whole in LDS, so it is also limited to reduction
+// lengths (H for L1, I for L2) whose rows fit; beyond that the tiled GEMM,
+// whose LDS use does not depend on K, takes small batches too.
+bool moe_use_skinny(int64_t S, int64_t E, int64_t H, int64_t I) {
+    return S <= (int64_t)kSkinnyBM * E && skinny_lds_bytes(H) <= kSkinnyMaxLds &&
+           skinny_lds_bytes(I) <= kSkinnyMaxLds;
+}
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     MoeLayout L;
@@ -108,7 +114,7 @@ const char* nvfp4_strerror(int status) {
     }
 }
 
-int nvfp4_version(void) { return (3 << 16) | 1; }
+int nvfp4_version(void) { return (4 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -290,9 +296,11 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return NVFP4_EINVAL;
     const int per_half = options ? options->w13_alpha_per_half : 0;
     const float* x_gs = options ? options->x_global_scale : nullptr;
+    uint16_t* gu_tap = options ? options->gate_up_tap : nullptr;
     if (per_half != 0 && per_half != 1) return NVFP4_EINVAL;
     if (options && options->reserved != 0) return NVFP4_EINVAL;
     if (x_gs && !aligned(x_gs, 4)) return NVFP4_EINVAL;
+    if (gu_tap && !aligned(gu_tap, 4)) return NVFP4_EINVAL;
     if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
     if (!w13 || !w13_sf || !w13_alpha || !w2 || !w2_sf || !w2_alpha) return NVFP4_EINVAL;
     if (T > 0 && (!x || !topk_ids || !topk_weights || !y)) return NVFP4_EINVAL;
@@ -329,7 +337,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     Tile* tiles = reinterpret_cast<Tile*>(ws + L.tiles);
     int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
     const int64_t S = T * topk;
-    const bool skinny = moe_use_skinny(S, E);
+    const bool skinny = moe_use_skinny(S, E, H, I);
     const int BM = skinny ? kSkinnyBM : kGemmBM;
     const int64_t max_tiles = moe_max_tiles(S, E, BM);
 
@@ -375,6 +383,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     p1.out_bf16 = act;
     p1.I = I;
     p1.amax_slot = amax + 1;
+    p1.gu_tap = gu_tap;
     NVFP4_TRY(skinny ? launch_skinny(p1, stream) : launch_gemm(p1, stream));
     // 4. requantize act (rows of valid slots only: offsets[E])
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_REQUANT));

@@ -402,6 +402,12 @@ void gemm_kernel(GemmParams p) {
                     // elements float32 cannot decide are redone in float64 after
                     // it, behind one branch that is rarely taken.
                     constexpr int RS = NT / 64;                   // row step of a thread
+                    // optional tap of the rounded gate | up values (same rows,
+                    // gate pair at column col, up pair at I + col)
+                    uint32_t* tap = p.gu_tap ? reinterpret_cast<uint32_t*>(
+                                                   p.gu_tap + (int64_t)(row_start + r0) * 2 * p.I + col)
+                                             : nullptr;
+                    const int64_t tstep = (int64_t)RS * p.I;      // RS rows of 2I bf16, in 4-byte units
                     int r = r0;
                     for (; r + 3 * RS < rows; r += 4 * RS, dst += 4 * dstep) {
                         float g[8], u[8], v[8];
@@ -412,7 +418,12 @@ void gemm_kernel(GemmParams p) {
                             u[2 * k] = bf16_to_f32(w[0] >> 16);
                             g[2 * k + 1] = bf16_to_f32(w[1] & 0xFFFFu);
                             u[2 * k + 1] = bf16_to_f32(w[1] >> 16);
+                            if (tap) {
+                                tap[k * tstep] = (w[0] & 0xFFFFu) | (w[1] << 16);
+                                tap[k * tstep + p.I / 2] = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
+                            }
                         }
+                        if (tap) tap += 4 * tstep;
                         // lanes with an element float32 cannot decide, as a
                         // wave mask (scalar ORs of the compare masks)
                         uint64_t redo = 0;
@@ -448,6 +459,11 @@ void gemm_kernel(GemmParams p) {
                     }
                     for (; r < rows; r += RS, dst += dstep) {
                         const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * GU_LD + 2 * cp);
+                        if (tap) {
+                            tap[0] = (w[0] & 0xFFFFu) | (w[1] << 16);
+                            tap[p.I / 2] = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
+                            tap += tstep;
+                        }
                         const uint32_t a = silu_mul_bf16x2(bf16_to_f32(w[0] & 0xFFFFu), bf16_to_f32(w[0] >> 16),
                                                            bf16_to_f32(w[1] & 0xFFFFu), bf16_to_f32(w[1] >> 16));
                         *dst = a;
@@ -536,13 +552,9 @@ hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     const int64_t mt = (MODE == kGemmDense) ? (p.M + BM - 1) / BM : p.max_tiles;
     const int64_t grid = mt * ntn;
     if (grid <= 0) return hipSuccess;
-    static bool configured = false;
-    if (!configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static std::atomic<int> lds_set[kMaxDevices];
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<MODE>), LDS_BYTES, lds_set);
+    if (e != hipSuccess) return e;
     gemm_kernel<MODE><<<(unsigned)grid, NT, LDS_BYTES, s>>>(p);
     return hipGetLastError();
 }

@@ -5,7 +5,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace nvfp4 {
+
+// Raise a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device. The attribute belongs to the (kernel, device) pair, so the largest
+// value set so far is remembered per device (one cache per kernel, indexed by
+// device); concurrent callers may both set it, which is harmless, and the
+// remembered maximum only grows.
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_dynamic_lds(const void* kernel, int bytes, std::atomic<int> (&done)[kMaxDevices]) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return e;
+    int cur = done[dev].load(std::memory_order_relaxed);
+    while (cur < bytes && !done[dev].compare_exchange_weak(cur, bytes, std::memory_order_release)) {
+    }
+    return hipSuccess;
+}
 
 // Tile descriptor of the grouped GEMMs: rows [row_start, row_start + row_count)
 // of the sorted slot order, all routed to `expert`.
@@ -148,12 +169,19 @@ struct GemmParams {
     float* out_f32;            // L2: (S, N)
     int64_t I;                 // L1: act columns (N = 2I)
     uint32_t* amax_slot;       // L1: act amax (atomic max of float bits)
+    uint16_t* gu_tap;          // L1: null, or (rows, 2I) bf16 gate | up values out
 };
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 // Weight-streaming variant for tiles of at most kSkinnyBM rows (L1 / L2 only).
+// It stages the tile's A rows whole in LDS: skinny_lds_bytes(K) must not
+// exceed kSkinnyMaxLds (K up to about 17,000).
 constexpr int kSkinnyBM = 16;
+constexpr int64_t kSkinnyMaxLds = 150 * 1024;
+__host__ __device__ inline int64_t skinny_lds_bytes(int64_t K) {
+    return (int64_t)kSkinnyBM * (pitch_q(K) + 16 + pitch_sf(K));
+}
 hipError_t launch_skinny(const GemmParams& p, hipStream_t s);
 
 }  // namespace nvfp4

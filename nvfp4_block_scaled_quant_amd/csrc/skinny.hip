@@ -296,9 +296,14 @@ void skinny_kernel(GemmParams p) {
 #pragma unroll
             for (int f = 0; f < GB; ++f) {
                 if (!ok[f]) continue;
-                const float g = bf16_to_f32(f32_to_bf16_rne(alpha * acc[f][i]));
-                const float u = bf16_to_f32(f32_to_bf16_rne(alpha_up * acc[f + GB][i]));
-                const uint32_t a = silu_mul_bf16(g, u);
+                const uint32_t gb = f32_to_bf16_rne(alpha * acc[f][i]);
+                const uint32_t ub = f32_to_bf16_rne(alpha_up * acc[f + GB][i]);
+                if (p.gu_tap) {
+                    uint16_t* t = p.gu_tap + prow * 2 * p.I + col0 + 16 * f + c;
+                    t[0] = (uint16_t)gb;
+                    t[p.I] = (uint16_t)ub;
+                }
+                const uint32_t a = silu_mul_bf16(bf16_to_f32(gb), bf16_to_f32(ub));
                 amax_bits = max(amax_bits, a & 0x7FFFu);
                 p.out_bf16[prow * p.I + col0 + 16 * f + c] = (uint16_t)a;
             }
@@ -325,16 +330,11 @@ template <int MODE>
 hipError_t launch_skinny_mode(const GemmParams& p, hipStream_t s) {
     const int64_t grid = p.max_tiles * skinny_slabs(MODE, p.I, p.N);
     if (grid <= 0) return hipSuccess;
-    const int64_t ldq = pitch_q(p.K), ldsf = pitch_sf(p.K);
-    const size_t lds = (size_t)SM * (ldq + 16 + ldsf);
-    if (lds > 150 * 1024) return hipErrorInvalidValue;
-    static size_t configured = 0;      // largest dynamic LDS size enabled so far
-    if (lds > configured) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        configured = lds;
-    }
+    const int64_t lds = skinny_lds_bytes(p.K);
+    if (lds > kSkinnyMaxLds) return hipErrorInvalidValue;
+    static std::atomic<int> lds_set[kMaxDevices];
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&skinny_kernel<MODE>), (int)lds, lds_set);
+    if (e != hipSuccess) return e;
     skinny_kernel<MODE><<<(unsigned)grid, NT, lds, s>>>(p);
     return hipGetLastError();
 }

@@ -152,8 +152,10 @@ def gpu_packed_weights(nv, L):
 
 
 def run_gpu_layer(nv, L, repeat=1, packed=None):
-    """Run nvfp4_moe_forward; return y bits and the workspace intermediates
-    (quantized operands cut to their unpadded widths)."""
+    """Run nvfp4_moe_forward `repeat` times, the last call with the gate/up
+    tap; return y bits of every call, the tapped gate/up values ("gu", sorted
+    rows) and the workspace intermediates (quantized operands cut to their
+    unpadded widths)."""
     import torch
     from conftest import to_dev, to_host
     d = {k: to_dev(L[k]) for k in ("x", "ids", "wts")}
@@ -165,10 +167,13 @@ def run_gpu_layer(nv, L, repeat=1, packed=None):
     nws = nv.moe_workspace_size(T, H, I, E, k)
     ws = torch.empty((nws,), dtype=torch.uint8, device="cuda")
     x_gs = to_dev(np.array([L["x_gs"]], np.float32)) if L.get("x_gs") is not None else None
+    I2 = 2 * I
+    tap = torch.zeros((T * k, I2), dtype=torch.bfloat16, device="cuda")
     ys = []
-    for _ in range(repeat):
+    for i in range(repeat):
         y = nv.moe_forward(d["x"], d["ids"], d["wts"], pw["w13"], pw["w13_sf"], pw["w13a"],
-                           pw["w2"], pw["w2_sf"], pw["w2a"], workspace=ws, x_gs=x_gs)
+                           pw["w2"], pw["w2_sf"], pw["w2a"], workspace=ws, x_gs=x_gs,
+                           gate_up_tap=tap if i == repeat - 1 else None)
         ys.append(to_host(y))
     torch.cuda.synchronize()
     lay = nv.moe_workspace_layout(T, H, I, E, k)
@@ -181,7 +186,7 @@ def run_gpu_layer(nv, L, repeat=1, packed=None):
         o = lay[name]
         return wsh[o:o + count * np.dtype(dtype).itemsize].view(dtype)
 
-    out = {"y": ys[-1], "ys": ys,
+    out = {"y": ys[-1], "ys": ys, "gu": to_host(tap),
            "xq": view("xq", np.uint8, T * ldq_h).reshape(T, ldq_h)[:, :H // 2],
            "xsf": view("xsf", np.uint8, T * ldsf_h).reshape(T, ldsf_h)[:, :H // 16],
            "gs1": view("gs1", np.float32, 1)[0], "gs2": view("gs2", np.float32, 1)[0],

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (3, 1)
+    assert nv.version() == (4, 0)
     for code in range(6):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
@@ -157,7 +157,9 @@ def test_moe_forward_ex_option_errors(nv):
     assert call(nv.MoeOptions(-1, 0, None)) == 1
     assert call(nv.MoeOptions(0, 0, A16 + 2)) == 1           # misaligned static scale
     assert call(nv.MoeOptions(0, 7, None)) == 1               # reserved must be 0
+    assert call(nv.MoeOptions(0, 0, None, A16 + 2)) == 1     # misaligned gate/up tap
     assert call(nv.MoeOptions(1, 0, A16)) == 3               # valid options, then the workspace
+    assert call(nv.MoeOptions(1, 0, A16, A16)) == 3
     assert call(nv.MoeOptions(1, 0, A16), T=0) == 3
 
 
