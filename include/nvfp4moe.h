@@ -84,7 +84,9 @@ typedef enum nvfp4_status {
     NVFP4_ESHAPE = 2,       /* a K dimension not a multiple of 16, topk > E, ... */
     NVFP4_EWORKSPACE = 3,   /* workspace missing, too small or misaligned */
     NVFP4_EHIP = 4,         /* a HIP call or kernel launch failed */
-    NVFP4_EDEVICE = 5       /* the current device is not gfx950 */
+    NVFP4_EDEVICE = 5,      /* the current device is not gfx950 */
+    NVFP4_ESCRATCH = 6      /* nvfp4_moe_forward_noalloc: the problem needs more
+                               than NVFP4_MOE_SCRATCH_BYTES of workspace */
 } nvfp4_status;
 
 /* Human-readable text of a status code (host string, static storage). */
@@ -332,6 +334,38 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
                          uint16_t* y, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, hipEvent_t* stage_events,
                          const nvfp4_moe_options* options);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_moe_forward_noalloc - nvfp4_moe_forward_ex for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * semantics and results as nvfp4_moe_forward_ex, minus the workspace: the
+ * library keeps it in a static device array of NVFP4_MOE_SCRATCH_BYTES
+ * (32 MiB) per GPU, held from the library's load until the process ends, and
+ * this call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine). 32 MiB covers decode-sized batches, e.g. up to about 110 tokens
+ * at top-8 with hidden 7168 and intermediate 3072; compare
+ * nvfp4_moe_workspace(T, H, I, E, topk) with NVFP4_MOE_SCRATCH_BYTES.
+ *
+ * Errors: those of nvfp4_moe_forward_ex, and NVFP4_ESCRATCH (before anything
+ * is enqueued) when nvfp4_moe_workspace(T, H, I, E, topk) exceeds
+ * NVFP4_MOE_SCRATCH_BYTES. The first call on a device looks up that device's
+ * copy of the array (a host-side runtime query, no allocation).
+ *
+ * Sharing: every call on one GPU uses that GPU's single array, which keeps
+ * the previous call's intermediates (no call relies on its contents: each
+ * writes what it reads). Calls that may overlap on one GPU (different
+ * streams, or graph replays in flight together) race on it and must be
+ * serialized by the caller. The intermediates are not exposed: use
+ * nvfp4_moe_forward with a workspace to inspect them.
+ * ------------------------------------------------------------------------ */
+#define NVFP4_MOE_SCRATCH_BYTES (32u << 20)
+int nvfp4_moe_forward_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                              const uint8_t* w13, const uint8_t* w13_sf, const float* w13_alpha,
+                              const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha,
+                              int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk,
+                              uint16_t* y, hipStream_t stream, hipEvent_t* stage_events,
+                              const nvfp4_moe_options* options);
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_route_topk - the router that produces the layer's topk_ids and

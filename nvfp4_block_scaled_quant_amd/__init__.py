@@ -14,7 +14,8 @@ mirror the C ABI in include/nvfp4moe.h:
     gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
     moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
                 w2, w2_sf, w2_alpha, workspace=None, stage_events=None,
-                x_gs=None) -> y          (w13_alpha (E,) or per half (E, 2))
+                x_gs=None, gate_up_tap=None) -> y   (w13_alpha (E,) or per half (E, 2))
+    moe_forward_noalloc(...)         -> y     the same without a workspace
     route_topk(logits, topk)         -> (topk_ids, topk_weights)
 
 The library must be built in-tree first (``python -m
@@ -56,7 +57,12 @@ _SIGS = {
                                      _int),
     "nvfp4_moe_forward_ex": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _sz, _vp, _vp, _vp], _int),
     "nvfp4_route_topk": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
+    "nvfp4_moe_forward_noalloc": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _vp, _vp], _int),
 }
+
+# NVFP4_MOE_SCRATCH_BYTES (include/nvfp4moe.h): the static workspace of
+# nvfp4_moe_forward_noalloc
+MOE_SCRATCH_BYTES = 32 << 20
 
 
 class MoeOptions(ctypes.Structure):
@@ -305,17 +311,10 @@ def moe_workspace_layout(T, H, I, E, topk):
     return dict(zip(WS_NAMES, list(arr)))
 
 
-def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
-                y=None, workspace=None, stage_events=None, x_gs=None, gate_up_tap=None):
-    """The five-stage NVFP4 expert layer. Weights in the packed layout
-    (prepack_weights of the canonical (E, H/2, 2I) and (E, I/2, H) tensors).
-
-    w13_alpha: (E,) one weight global scale per expert, or (E, 2) per half
-    (gate, up). x_gs: None (dynamic gs1) or a float32 (1,) static gs1.
-    gate_up_tap: None, or a bf16 (T * topk, 2I) tensor that receives the
-    rounded L1 output (sorted rows, gate | up), for stage-by-stage checks.
-    stage_events: None or a StageEvents; returns y (T, H) bf16.
-    """
+def _moe_args(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha, y, x_gs,
+              gate_up_tap):
+    """Checks shared by moe_forward and moe_forward_noalloc; returns the sizes,
+    y and the options struct (None when every option is at its default)."""
     _need(x, torch.bfloat16, "x", 2)
     dev = x.device
     _need(topk_ids, torch.int32, "topk_ids", 2, dev)
@@ -344,22 +343,52 @@ def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2
     y = _out(y, (T, H), torch.bfloat16, dev, "y")
     if gate_up_tap is not None:
         _out(gate_up_tap, (T * topk, 2 * I), torch.bfloat16, dev, "gate_up_tap")
-    workspace = _workspace(workspace, moe_workspace_size(T, H, I, E, topk), dev)
-    ev = stage_events.handles if stage_events is not None else None
     per_half = w13_alpha.dim() == 2
-    if not per_half and x_gs is None and gate_up_tap is None:
-        _check(_lib.nvfp4_moe_forward(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
-                                      _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
-                                      _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
-                                      _nbytes(workspace), _stream(), ev), "nvfp4_moe_forward")
-        return y
-    opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None,
-                      gate_up_tap.data_ptr() if gate_up_tap is not None else None)
-    _check(_lib.nvfp4_moe_forward_ex(_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13),
-                                     _ptr(w13_sf), _ptr(w13_alpha), _ptr(w2), _ptr(w2_sf),
-                                     _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
-                                     _nbytes(workspace), _stream(), ev, ctypes.byref(opts)),
-           "nvfp4_moe_forward_ex")
+    opts = None
+    if per_half or x_gs is not None or gate_up_tap is not None:
+        opts = MoeOptions(1 if per_half else 0, 0, x_gs.data_ptr() if x_gs is not None else None,
+                          gate_up_tap.data_ptr() if gate_up_tap is not None else None)
+    return T, H, I, E, topk, y, opts
+
+
+def moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
+                y=None, workspace=None, stage_events=None, x_gs=None, gate_up_tap=None):
+    """The five-stage NVFP4 expert layer. Weights in the packed layout
+    (prepack_weights of the canonical (E, H/2, 2I) and (E, I/2, H) tensors).
+
+    w13_alpha: (E,) one weight global scale per expert, or (E, 2) per half
+    (gate, up). x_gs: None (dynamic gs1) or a float32 (1,) static gs1.
+    gate_up_tap: None, or a bf16 (T * topk, 2I) tensor that receives the
+    rounded L1 output (sorted rows, gate | up), for stage-by-stage checks.
+    stage_events: None or a StageEvents; returns y (T, H) bf16.
+    """
+    T, H, I, E, topk, y, opts = _moe_args(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2,
+                                          w2_sf, w2_alpha, y, x_gs, gate_up_tap)
+    workspace = _workspace(workspace, moe_workspace_size(T, H, I, E, topk), x.device)
+    ev = stage_events.handles if stage_events is not None else None
+    args = (_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13), _ptr(w13_sf), _ptr(w13_alpha),
+            _ptr(w2), _ptr(w2_sf), _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _ptr(workspace),
+            _nbytes(workspace), _stream(), ev)
+    if opts is None:
+        _check(_lib.nvfp4_moe_forward(*args), "nvfp4_moe_forward")
+    else:
+        _check(_lib.nvfp4_moe_forward_ex(*args, ctypes.byref(opts)), "nvfp4_moe_forward_ex")
+    return y
+
+
+def moe_forward_noalloc(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha,
+                        y=None, stage_events=None, x_gs=None, gate_up_tap=None):
+    """moe_forward without a workspace: the library's static per-GPU scratch
+    (MOE_SCRATCH_BYTES) holds the intermediates and the call allocates
+    nothing on the device (pass y to allocate nothing at all). Calls that
+    overlap on one GPU share that scratch and must not run concurrently."""
+    T, H, I, E, topk, y, opts = _moe_args(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2,
+                                          w2_sf, w2_alpha, y, x_gs, gate_up_tap)
+    ev = stage_events.handles if stage_events is not None else None
+    _check(_lib.nvfp4_moe_forward_noalloc(
+        _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w13), _ptr(w13_sf), _ptr(w13_alpha),
+        _ptr(w2), _ptr(w2_sf), _ptr(w2_alpha), T, H, I, E, topk, _ptr(y), _stream(), ev,
+        ctypes.byref(opts) if opts is not None else None), "nvfp4_moe_forward_noalloc")
     return y
 
 

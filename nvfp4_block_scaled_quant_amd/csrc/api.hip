@@ -2,6 +2,7 @@
 // carving and the launch sequence. Declarations and contracts: include/nvfp4moe.h.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nvfp4moe.h"
 #include "launch.hpp"
@@ -17,12 +18,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // 0 = not checked, 1 = gfx950, 2 = other
-std::atomic<int> g_device_ok[64];
+std::atomic<int> g_device_ok[kMaxDevices];
 
 int check_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return NVFP4_EHIP;
-    if (dev < 0 || dev >= 64) return NVFP4_EDEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_EDEVICE;
     int st = g_device_ok[dev].load(std::memory_order_relaxed);
     if (st == 0) {
         hipDeviceProp_t prop;
@@ -98,6 +99,35 @@ bool moe_shape_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     return true;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free variant of the layer keeps its workspace in a file-scope
+// device array: every GPU the library runs on holds one copy of it (from the
+// code object's load until the process ends). On the host `scratch` only
+// names the symbol; its device address, which differs per device, comes from
+// hipGetSymbolAddress with that device current, taken once per device on the
+// entry point's first call there and kept.
+static __device__ __align__(256) uint8_t scratch[NVFP4_MOE_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return NVFP4_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return NVFP4_EDEVICE;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return NVFP4_EHIP;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,11 +140,14 @@ const char* nvfp4_strerror(int status) {
         case NVFP4_EWORKSPACE: return "workspace missing, misaligned (256 bytes) or too small";
         case NVFP4_EHIP: return "HIP runtime error or kernel launch failure";
         case NVFP4_EDEVICE: return "current device is not an MI355X-class gfx950 GPU";
+        case NVFP4_ESCRATCH:
+            return "the layer's workspace exceeds the allocation-free entry point's static scratch "
+                   "(NVFP4_MOE_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
 
-int nvfp4_version(void) { return (4 << 16) | 0; }
+int nvfp4_version(void) { return (4 << 16) | 1; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -412,6 +445,27 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     NVFP4_TRY(launch_combine(o2, slot_row, topk_weights, T, (int)topk, H, y, stream));
     NVFP4_TRY(mark(NVFP4_MOE_NUM_STAGES));
     return NVFP4_OK;
+}
+
+int nvfp4_moe_forward_noalloc(const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                              const uint8_t* w13, const uint8_t* w13_sf, const float* w13_alpha,
+                              const uint8_t* w2, const uint8_t* w2_sf, const float* w2_alpha,
+                              int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk, uint16_t* y,
+                              hipStream_t stream, hipEvent_t* stage_events,
+                              const nvfp4_moe_options* options) {
+    // the shape checks of nvfp4_moe_forward_ex first, so that a bad shape is
+    // reported as such and not as a scratch overflow
+    if (T < 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return NVFP4_EINVAL;
+    if (!moe_shape_ok(T, H, I, E, topk)) return NVFP4_ESHAPE;
+    if (moe_layout(T, H, I, E, topk).total > (size_t)NVFP4_MOE_SCRATCH_BYTES) return NVFP4_ESCRATCH;
+    int dv = check_device();
+    if (dv) return dv;
+    void* ws = nullptr;
+    const int st = scratch_address(&ws);
+    if (st) return st;
+    return nvfp4_moe_forward_ex(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha, w2, w2_sf, w2_alpha, T,
+                                H, I, E, topk, y, ws, (size_t)NVFP4_MOE_SCRATCH_BYTES, stream,
+                                stage_events, options);
 }
 
 // ---------------------------------------------------------------------------

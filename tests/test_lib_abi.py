@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (4, 0)
-    for code in range(6):
+    assert nv.version() == (4, 1)
+    for code in range(7):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
 
@@ -161,6 +161,23 @@ def test_moe_forward_ex_option_errors(nv):
     assert call(nv.MoeOptions(1, 0, A16)) == 3               # valid options, then the workspace
     assert call(nv.MoeOptions(1, 0, A16, A16)) == 3
     assert call(nv.MoeOptions(1, 0, A16), T=0) == 3
+
+
+def test_moe_forward_noalloc_argument_errors(nv):
+    # validated on the host before the scratch array or any device is touched
+    f = lib(nv).nvfp4_moe_forward_noalloc
+    ptrs9 = [p(A16)] * 9
+
+    def call(T, H=7168, I=3072, E=48, k=8):
+        return f(*ptrs9, T, H, I, E, k, p(A16), None, None, None)
+
+    assert call(4096) == 6                     # the prefill batch needs ~1.2 GB: beyond the scratch
+    assert call(-1) == 1
+    assert call(8, k=49) == 2                  # topk > E
+    assert call(8, H=7000) == 2
+    assert nv.moe_workspace_size(8, 7168, 3072, 48, 8) <= nv.MOE_SCRATCH_BYTES
+    assert nv.moe_workspace_size(4096, 7168, 3072, 48, 8) > nv.MOE_SCRATCH_BYTES
+    assert "scratch" in nv.strerror(6)
 
 
 def test_quantize_static_argument_errors(nv):
