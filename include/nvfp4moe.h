@@ -29,10 +29,10 @@
  *   weights               column n of W[e], packed along K like an A row
  *                         (byte kh = W[2kh][n] | W[2kh+1][n] << 4), zero-padded
  *                         to pitch_q(K) bytes; rows are stored in blocks of 16
- *                         and inside a block by 128-element K step: byte kh of
- *                         row n is at
+ *                         and inside a block by 64-element half step (32 bytes
+ *                         of each of the 16 rows): byte kh of row n is at
  *                           e * N * pitch_q(K) + (n / 16) * 16 * pitch_q(K)
- *                           + (kh / 64) * 1024 + (n % 16) * 64 + kh % 64
+ *                           + (kh / 32) * 512 + (n % 16) * 32 + kh % 32
  *                w_sf_t   E * N * pitch_wsf(K) E4M3 bytes, zero-padded, in the
  *                         same 16-row blocks, by groups of four K steps (st =
  *                         g / 8 is the step of scale group g): scale g of row
@@ -46,10 +46,13 @@
  *   pitch_sf(K)  = K/16 rounded up to a multiple of 8 bytes (activation scales)
  *   pitch_wsf(K) = 32 bytes per group of four steps: pitch_q(K) / 64 rounded up
  *                  to a multiple of 4, times 8
+ *   pitch_h(K)   = 4 * pitch_q(K): bytes of a row of f16 values, K rounded up
+ *                  to whole 128-element steps
  *   The packed weights are the canonical ones with every matrix byte-transposed
  *   (the pages' GEMM took its weight operand column-major) and blocked so that
- *   one K step of 16 rows, the unit a matrix-core operand load covers, is one
- *   contiguous kilobyte. They are made once, at load time, by
+ *   one 64-element half step of 16 rows (what a tiled-GEMM stage holds) is 512
+ *   contiguous bytes and one 128-element K step (what a streaming load covers)
+ *   one contiguous kilobyte. They are made once, at load time, by
  *   nvfp4_prepack_weights and are what the GEMMs read. N % 16 == 0.
  *   w13 is the plain concatenation [gate; up] along N: columns [0, I) are the
  *   gate projection, [I, 2I) the up projection (rows [0, I) / [I, 2I) packed).
@@ -204,20 +207,29 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
  *   out[m][n] = bf16( (a_gs[0] * b_alpha[0]) * sum_k deqA[m][k] * deqB[k][n] )
  *
  *   aq (M, K/2), asf (M, K/16): the quantized activation (nvfp4_quantize),
- *           aq 16-byte and asf 8-byte aligned
+ *           aq 8-byte aligned
  *   a_gs    one float32, the activation's global scale
- *   bq (N * K/2 bytes), bsf (N * pitch_wsf(K) bytes): one packed weight
- *           matrix (nvfp4_prepack_weights with E = 1; for K % 128 == 0,
- *           pitch_q(K) is exactly K/2), bq 16-byte and bsf 8-byte aligned
+ *   bq (N * pitch_q(K) bytes), bsf (N * pitch_wsf(K) bytes): one packed weight
+ *           matrix (nvfp4_prepack_weights with E = 1), bq 16-byte and bsf
+ *           8-byte aligned
  *   b_alpha one float32
  *   out (M, N) bf16
  * Products of dequantized elements are exact; the sum is float32; the alpha
  * product and its multiply are float32; the one bf16 rounding is the last step.
- * K % 128 == 0, N % 16 == 0, M * K/2 and N * K/2 below 2^31. No workspace.
+ * K % 16 == 0, N % 16 == 0, M * pitch_h(K) and N * pitch_q(K) below 2^31
+ * (pitch_h(K) = 4 * pitch_q(K)), else NVFP4_ESHAPE.
+ *
+ * Workspace: nvfp4_gemm_workspace(M, N, K) bytes (M * pitch_h(K) rounded up
+ * to 256), 256-byte aligned; it receives A in its exact f16 form (e2m1 *
+ * e4m3 per element, rows padded with zeros to whole 128-element steps), the
+ * operand the matrix cores read. nvfp4_gemm_workspace returns 0 for invalid
+ * sizes.
  * ------------------------------------------------------------------------ */
+size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
                const uint8_t* bq, const uint8_t* bsf, const float* b_alpha,
-               int64_t M, int64_t N, int64_t K, uint16_t* out, hipStream_t stream);
+               int64_t M, int64_t N, int64_t K, uint16_t* out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_moe_forward - the five-stage NVFP4 expert layer on one GPU's experts
@@ -241,7 +253,7 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *                 the scale tensors 8-byte aligned
  *   y             (T, H) bf16 out
  *   H % 16 == 0, I % 16 == 0, 1 <= topk <= E, T >= 0; each of
- *   2I * pitch_q(H), H * pitch_q(I), T * pitch_q(H), T * topk * pitch_q(I)
+ *   2I * pitch_q(H), H * pitch_q(I), T * pitch_h(H), T * topk * pitch_h(I)
  *   below 2^31 (32-bit buffer offsets), else NVFP4_ESHAPE.
  *
  * Workspace: nvfp4_moe_workspace(T, H, I, E, topk) bytes, 256-byte aligned.
@@ -279,7 +291,14 @@ enum {
     NVFP4_MOE_WS_AQ = 9,            /* (S, pitch_q(I)) bytes, sorted rows, first I/2 used */
     NVFP4_MOE_WS_ASF = 10,          /* (S, pitch_sf(I)) bytes, sorted rows, first I/16 used */
     NVFP4_MOE_WS_O2 = 11,           /* float32 (S, H), sorted rows, weight not applied */
-    NVFP4_MOE_WS_NUM = 12
+    NVFP4_MOE_WS_XH = 12,           /* f16 (T, pitch_h(H) / 2): the exact values of xq
+                                       (e2m1 * e4m3), read by the tiled L1 GEMM;
+                                       empty when the batch takes the weight-
+                                       streaming kernels (at most 16 slots per
+                                       expert on average) */
+    NVFP4_MOE_WS_AH = 13,           /* f16 (S, pitch_h(I) / 2): the exact values of
+                                       aq, sorted rows; empty like XH */
+    NVFP4_MOE_WS_NUM = 14
 };
 
 size_t nvfp4_moe_workspace(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk);

@@ -11,7 +11,7 @@ mirror the C ABI in include/nvfp4moe.h:
     operand_pitches(K)               -> (ldq, ldsf, ldwsf)
     packed_shapes(E, K, N)           -> shapes of the packed weight tensors
     prepack_weights(q, sf)           -> (q_t, sf_t)       packed layout the GEMMs read
-    gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16)
+    gemm(aq, asf, a_gs, bq_t, bsf_t, b_alpha) -> out (bf16), K % 16 == 0
     moe_forward(x, topk_ids, topk_weights, w13, w13_sf, w13_alpha,
                 w2, w2_sf, w2_alpha, workspace=None, stage_events=None,
                 x_gs=None, gate_up_tap=None) -> y   (w13_alpha (E,) or per half (E, 2))
@@ -47,7 +47,8 @@ _SIGS = {
     "nvfp4_quantize_weights": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "nvfp4_operand_pitches": ([_i64] + [ctypes.POINTER(_i64)] * 3, _int),
     "nvfp4_prepack_weights": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp], _int),
-    "nvfp4_gemm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp], _int),
+    "nvfp4_gemm_workspace": ([_i64, _i64, _i64], _sz),
+    "nvfp4_gemm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp], _int),
     "nvfp4_moe_workspace": ([_i64, _i64, _i64, _i64, _i64], _sz),
     "nvfp4_moe_workspace_layout": ([_i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_sz)], _int),
     "nvfp4_moe_forward": ([_vp] * 9 + [_i64] * 5 + [_vp, _vp, _sz, _vp, _vp], _int),
@@ -82,7 +83,7 @@ EXPORTED = tuple(_SIGS)
 STAGES = ("route", "quant_x", "l1", "requant", "l2", "combine")
 NUM_EVENTS = len(STAGES) + 1
 WS_NAMES = ("xq", "xsf", "gs1", "gs2", "counts", "offsets", "sorted_slot", "slot_row",
-            "act", "aq", "asf", "o2")
+            "act", "aq", "asf", "o2", "xh", "ah")
 
 
 class Nvfp4Error(RuntimeError):
@@ -246,14 +247,15 @@ def operand_pitches(K):
 
 def packed_shapes(E, K, N):
     """Shapes of the packed weight tensors of E matrices (K, N), in 16-row
-    blocks: data (E, N/16, steps, 16, 64), one 128-element K step of the
-    block's 16 rows after another, steps = ldq / 64; scales (E, N/16, quads,
-    16, 32), quads = ldwsf / 32: per group of four K steps, row, pair of scale
-    groups (4), step of the four (4), then the pair's two bytes."""
+    blocks: data (E, N/16, halves, 16, 32), one 64-element half step of the
+    block's 16 rows after another, halves = ldq / 32; scales (E, N/16, quads,
+    16, 32), quads = ldwsf / 32: per group of four 128-element K steps, row,
+    pair of scale groups (4), step of the four (4), then the pair's two
+    bytes."""
     ldq, _, ldwsf = operand_pitches(K)
     if N % 16:
         raise ValueError("packed weights need N % 16 == 0")
-    return (E, N // 16, ldq // 64, 16, 64), (E, N // 16, ldwsf // 32, 16, 32)
+    return (E, N // 16, ldq // 32, 16, 32), (E, N // 16, ldwsf // 32, 16, 32)
 
 
 def prepack_weights(q, sf):
@@ -273,10 +275,11 @@ def prepack_weights(q, sf):
     return q_t, sf_t
 
 
-def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
+def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None, workspace=None):
     """Block-scaled NVFP4 GEMM of one expert: A (M, K/2) + (M, K/16) times one
-    packed weight matrix bq (N/16, K/128, 16, 64) + bsf (N/16, quads, 16, 32)
-    (packed_shapes with E dropped) -> bf16 (M, N). K % 128 == 0."""
+    packed weight matrix bq (N/16, halves, 16, 32) + bsf (N/16, quads, 16, 32)
+    (packed_shapes with E dropped) -> bf16 (M, N). K % 16 == 0. The workspace
+    (nvfp4_gemm_workspace bytes) receives A's exact f16 values."""
     _need(aq, torch.uint8, "aq")
     for t, n, d in ((asf, "asf", torch.uint8), (bq, "bq", torch.uint8),
                     (bsf, "bsf", torch.uint8), (a_gs, "a_gs", torch.float32),
@@ -285,16 +288,19 @@ def gemm(aq, asf, a_gs, bq, bsf, b_alpha, out=None):
     if a_gs.numel() < 1 or b_alpha.numel() < 1:
         raise ValueError("gemm: a_gs and b_alpha must hold one float32 each")
     if aq.dim() != 2 or bq.dim() != 4:
-        raise ValueError("gemm: aq must be (M, K/2) and bq (N/16, K/128, 16, 64)")
+        raise ValueError("gemm: aq must be (M, K/2) and bq (N/16, halves, 16, 32)")
     M = aq.shape[0]
     K = aq.shape[1] * 2
     N = bq.shape[0] * 16
-    if (K % 128 or tuple(bq.shape) != (N // 16, K // 128, 16, 64) or asf.shape != (M, K // 16)
-            or tuple(bsf.shape) != packed_shapes(1, K, N)[1][1:]):
+    if K % 16:
+        raise ValueError("gemm: K must be a multiple of 16")
+    shq, shs = packed_shapes(1, K, N)
+    if tuple(bq.shape) != shq[1:] or asf.shape != (M, K // 16) or tuple(bsf.shape) != shs[1:]:
         raise ValueError("operand shapes do not match")
     out = _out(out, (M, N), torch.bfloat16, aq.device, "out")
+    ws = _workspace(workspace, max(1, _lib.nvfp4_gemm_workspace(M, N, K)), aq.device)
     _check(_lib.nvfp4_gemm(_ptr(aq), _ptr(asf), _ptr(a_gs), _ptr(bq), _ptr(bsf), _ptr(b_alpha),
-                           M, N, K, _ptr(out), _stream()), "nvfp4_gemm")
+                           M, N, K, _ptr(out), _ptr(ws), _nbytes(ws), _stream()), "nvfp4_gemm")
     return out
 
 

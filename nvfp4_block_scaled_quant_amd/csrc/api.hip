@@ -70,11 +70,14 @@ bool moe_use_skinny(int64_t S, int64_t E, int64_t H, int64_t I) {
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     MoeLayout L;
     const int64_t S = T * topk;
-    // quantized GEMM operands use the padded row pitches pitch_q / pitch_sf
+    // quantized GEMM operands use the padded row pitches pitch_q / pitch_sf;
+    // their f16 forms (pitch_h) exist only for the tiled GEMMs
+    const bool tiled = !moe_use_skinny(S, E, H, I);
     const size_t sizes[NVFP4_MOE_WS_NUM] = {
         (size_t)(T * pitch_q(H)), (size_t)(T * pitch_sf(H)), 4, 4,
         (size_t)(4 * E),      (size_t)(4 * (E + 1)), (size_t)(4 * S), (size_t)(4 * S),
-        (size_t)(2 * S * I),  (size_t)(S * pitch_q(I)), (size_t)(S * pitch_sf(I)), (size_t)(4 * S * H)};
+        (size_t)(2 * S * I),  (size_t)(S * pitch_q(I)), (size_t)(S * pitch_sf(I)), (size_t)(4 * S * H),
+        tiled ? (size_t)(T * pitch_h(H)) : 0, tiled ? (size_t)(S * pitch_h(I)) : 0};
     size_t cur = 0;
     for (int i = 0; i < NVFP4_MOE_WS_NUM; ++i) {
         L.off[i] = cur;
@@ -96,6 +99,10 @@ bool moe_shape_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     if (H % 16 || I % 16 || topk > E || E > kMaxExperts) return false;
     if (T > (int64_t)1 << 24 || H > (int64_t)1 << 20 || I > (int64_t)1 << 20) return false;
     if (T * topk >= ((int64_t)1 << 31)) return false;
+    // 32-bit buffer offsets: every GEMM operand stays below 2 GiB
+    if (2 * I * pitch_q(H) >= 0x7FFFFFFF || H * pitch_q(I) >= 0x7FFFFFFF ||
+        T * pitch_h(H) >= 0x7FFFFFFF || T * topk * pitch_h(I) >= 0x7FFFFFFF)
+        return false;
     return true;
 }
 
@@ -147,7 +154,7 @@ const char* nvfp4_strerror(int status) {
     }
 }
 
-int nvfp4_version(void) { return (4 << 16) | 1; }
+int nvfp4_version(void) { return (5 << 16) | 0; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace(int64_t M, int64_t K) {
@@ -266,23 +273,35 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
 }
 
 // ---------------------------------------------------------------------------
+size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
+    (void)N;
+    if (M < 0 || K <= 0 || K % 16) return 0;
+    return align_up((size_t)((M > 0 ? M : 1) * pitch_h(K)));
+}
+
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const uint8_t* bq,
                const uint8_t* bsf, const float* b_alpha, int64_t M, int64_t N, int64_t K,
-               uint16_t* out, hipStream_t stream) {
+               uint16_t* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (M < 0 || N <= 0 || K <= 0) return NVFP4_EINVAL;
-    if (K % 128 || N % 16) return NVFP4_ESHAPE;
+    if (K % 16 || N % 16) return NVFP4_ESHAPE;
+    if (M * pitch_h(K) >= 0x7FFFFFFF || N * pitch_q(K) >= 0x7FFFFFFF) return NVFP4_ESHAPE;
     if (M == 0) return NVFP4_OK;
     if (!aq || !asf || !a_gs || !bq || !bsf || !b_alpha || !out) return NVFP4_EINVAL;
-    if (!aligned(aq, 16) || !aligned(asf, 8) || !aligned(bq, 16) || !aligned(bsf, 8) ||
-        !aligned(out, 2) || !aligned(a_gs, 4) || !aligned(b_alpha, 4))
+    if (!aligned(aq, 8) || !aligned(bq, 16) || !aligned(bsf, 8) || !aligned(out, 2) || !aligned(a_gs, 4) ||
+        !aligned(b_alpha, 4))
         return NVFP4_EINVAL;
-    if (M * (K / 2) >= 0x7FFFFFFF || N * (K / 2) >= 0x7FFFFFFF) return NVFP4_ESHAPE;
+    if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < nvfp4_gemm_workspace(M, N, K))
+        return NVFP4_EWORKSPACE;
     int dv = check_device();
     if (dv) return dv;
+    // the A operand in its exact f16 form, rows padded to whole K steps
+    uint16_t* ah = static_cast<uint16_t*>(workspace);
+    NVFP4_TRY(launch_dequant_rows_f16(aq, asf, M, K, ah, stream));
     GemmParams p = {};
     p.mode = kGemmDense;
     p.aq = aq;
     p.asf = asf;
+    p.ah = ah;
     p.M = M;
     p.a_rows = M;
     p.bq = bq;
@@ -343,9 +362,6 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     if (!aligned(w13, 16) || !aligned(w2, 16) || !aligned(w13_sf, 8) || !aligned(w2_sf, 8) ||
         !aligned(w13_alpha, 4) || !aligned(w2_alpha, 4))
         return NVFP4_EINVAL;
-    if (2 * I * pitch_q(H) >= 0x7FFFFFFF || H * pitch_q(I) >= 0x7FFFFFFF ||
-        T * pitch_q(H) >= 0x7FFFFFFF || T * topk * pitch_q(I) >= 0x7FFFFFFF)
-        return NVFP4_ESHAPE;
     const MoeLayout L = moe_layout(T, H, I, E, topk);
     if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total)
         return NVFP4_EWORKSPACE;
@@ -366,6 +382,8 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     uint8_t* aq = ws + L.off[NVFP4_MOE_WS_AQ];
     uint8_t* asf = ws + L.off[NVFP4_MOE_WS_ASF];
     float* o2 = reinterpret_cast<float*>(ws + L.off[NVFP4_MOE_WS_O2]);
+    uint16_t* xh = reinterpret_cast<uint16_t*>(ws + L.off[NVFP4_MOE_WS_XH]);
+    uint16_t* ah = reinterpret_cast<uint16_t*>(ws + L.off[NVFP4_MOE_WS_AH]);
     uint32_t* amax = reinterpret_cast<uint32_t*>(ws + L.amax);
     Tile* tiles = reinterpret_cast<Tile*>(ws + L.tiles);
     int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
@@ -390,7 +408,8 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
         NVFP4_TRY(launch_zero_u32(amax, 1, stream));
         NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
     }
-    const SmallQuant sq = {x, x_gs, amax_pass ? amax : nullptr, T, H, xq, pitch_q(H), xsf, pitch_sf(H), gs1};
+    const SmallQuant sq = {x,   x_gs,        amax_pass ? amax : nullptr, T, H, xq, pitch_q(H), xsf,
+                           pitch_sf(H), gs1, skinny ? nullptr : xh};
     NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
                            slot_row, tiles, num_tiles, amax + 1, 1, &sq, stream));
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
@@ -400,6 +419,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     p1.mode = kGemmL1;
     p1.aq = xq;
     p1.asf = xsf;
+    p1.ah = xh;
     p1.a_rows = T;
     p1.a_gather = sorted_slot;
     p1.topk = (int)topk;
@@ -421,13 +441,14 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     // 4. requantize act (rows of valid slots only: offsets[E])
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_REQUANT));
     NVFP4_TRY(launch_quant_rows(act, S, I, offsets + E, amax + 1, aq, pitch_q(I), asf, pitch_sf(I), gs2,
-                                stream));
+                                stream, nullptr, skinny ? nullptr : ah));
     // 5a. L2 grouped GEMM
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L2));
     GemmParams p2 = {};
     p2.mode = kGemmL2;
     p2.aq = aq;
     p2.asf = asf;
+    p2.ah = ah;
     p2.a_rows = S;
     p2.bq = w2;
     p2.bsf = w2_sf;

@@ -289,6 +289,28 @@ __device__ __forceinline__ uint32_t quantize_block16(const uint32_t (&w)[8], con
 }
 
 // ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    return v;
+}
+
+// Byte transpose of a 4x4 block held in 4 words: in r[i] byte j = M[i][j];
+// out c[j] byte i = M[i][j].
+__device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&c)[4]) {
+    const uint32_t t01lo = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
+    const uint32_t t01hi = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+    const uint32_t t23lo = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
+    const uint32_t t23hi = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+    c[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
+    c[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+    c[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+    c[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
+}
+
+// ---------------------------------------------------------------------------
 // Dequantization for the MFMA operands.
 // The FP4 -> f16 conversion applies only the exponent of its float scale, so
 // it is given 2^8, and the E4M3 scale enters as an f16 multiply: shifting an
@@ -313,36 +335,28 @@ __device__ __forceinline__ half8_t dequant8(uint32_t word, half2_t sp) {
     return r;
 }
 
-// ---------------------------------------------------------------------------
-// Reductions
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-    return v;
+// The exact f16 values of one quantized 16-element block (8 packed bytes in
+// two words, its scale byte) to 32 bytes at dst (16-byte aligned).
+__device__ __forceinline__ void store_block_f16(uint8_t* __restrict__ dst, uint32_t p0, uint32_t p1,
+                                                uint32_t code) {
+    const half2_t sp = scale_pair(code);
+    half8_t* d = reinterpret_cast<half8_t*>(dst);
+    d[0] = dequant8(p0, sp);
+    d[1] = dequant8(p1, sp);
 }
 
-// Byte transpose of a 4x4 block held in 4 words: in r[i] byte j = M[i][j];
-// out c[j] byte i = M[i][j].
-__device__ __forceinline__ void transpose4x4(const uint32_t (&r)[4], uint32_t (&c)[4]) {
-    const uint32_t t01lo = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);
-    const uint32_t t01hi = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
-    const uint32_t t23lo = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);
-    const uint32_t t23hi = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
-    c[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
-    c[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-    c[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-    c[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
-}
-
-// Quantize block b of a row-major (rows, K) bf16 matrix (groups = K / 16
-// blocks per row) into rows of pitch ldq (packed) and ldsf (scales).
-// Block b (row b / groups, group b % groups) of a row-major bf16 matrix whose
-// 16 elements v0, v1 (8 bf16 pairs) are already loaded: quantize and store it.
+// Block b of a row-major (rows, K) bf16 matrix (groups = K / 16 blocks per
+// row) whose 16 elements v0, v1 (8 bf16 pairs) are already loaded: quantize
+// it and store the packed bytes and scale (rows of pitch ldq / ldsf) and,
+// when h is not null, its exact f16 values (rows of pitch_h(K) = 4 * ldq
+// bytes). Each row's padding up to the pitches is written as zeros by the
+// thread of its last block, so that a GEMM reading whole K steps sees zero
+// data and scales there.
 __device__ __forceinline__ void quantize_row_block_loaded(u32x4 v0, u32x4 v1, int64_t b,
                                                           int64_t groups, const QuantScales& qs,
                                                           uint8_t* __restrict__ q, int64_t ldq,
-                                                          uint8_t* __restrict__ sf, int64_t ldsf) {
+                                                          uint8_t* __restrict__ sf, int64_t ldsf,
+                                                          uint8_t* __restrict__ h) {
     const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
     uint32_t packed[2];
     const uint32_t code = quantize_block16(w, qs, packed);
@@ -352,20 +366,24 @@ __device__ __forceinline__ void quantize_row_block_loaded(u32x4 v0, u32x4 v1, in
     const int64_t r = b / groups, g = b - r * groups;
     *reinterpret_cast<u32x2*>(q + r * ldq + g * 8) = out;
     sf[r * ldsf + g] = (uint8_t)code;
+    const int64_t ldh = 4 * ldq;
+    if (h) store_block_f16(h + r * ldh + g * 32, packed[0], packed[1], code);
     if (g == groups - 1) {
-        // the row's padding up to the pitches is written as zeros, so that a
-        // GEMM reading whole 128-element steps sees zero scales and data there
         for (int64_t j = groups * 8; j < ldq; j += 8) *reinterpret_cast<u32x2*>(q + r * ldq + j) = (u32x2){0u, 0u};
         for (int64_t j = groups; j < ldsf; ++j) sf[r * ldsf + j] = 0;
+        if (h)
+            for (int64_t j = groups * 32; j < ldh; j += 16)
+                *reinterpret_cast<u32x4*>(h + r * ldh + j) = (u32x4){0u, 0u, 0u, 0u};
     }
 }
 
 __device__ __forceinline__ void quantize_row_block(const uint16_t* __restrict__ x, int64_t b,
                                                    int64_t groups, const QuantScales& qs,
                                                    uint8_t* __restrict__ q, int64_t ldq,
-                                                   uint8_t* __restrict__ sf, int64_t ldsf) {
+                                                   uint8_t* __restrict__ sf, int64_t ldsf,
+                                                   uint8_t* __restrict__ h) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
-    quantize_row_block_loaded(src[0], src[1], b, groups, qs, q, ldq, sf, ldsf);
+    quantize_row_block_loaded(src[0], src[1], b, groups, qs, q, ldq, sf, ldsf, h);
 }
 
 }  // namespace nvfp4

@@ -8,40 +8,49 @@
 // accumulation sums exact products; the global scales are applied once, as
 // float32 alpha, in the epilogue. gfx950's FP4 MFMAs take power-of-two (E8M0)
 // scales per 32 elements and cannot carry an E4M3 scale per 16 elements
-// exactly, so the operands are dequantized in registers and fed to
-// v_mfma_f32_32x32x16_f16.
+// exactly, so the operands are fed to v_mfma_f32_32x32x16_f16 as f16.
 //
-// Operands. A rows and B rows (one per weight column: the weights in the
-// byte-transposed layout, as the pages' GEMM consumed B column-major) are
-// both K-packed, 64 bytes per 128-element K step, with their E4M3 scales
-// alongside; B comes in 16-row blocks whose K steps are contiguous (1 KB per
-// step), so every load instruction of B reads one contiguous kilobyte. Tiles
-// move from HBM to LDS by buffer loads that write LDS directly (no staging
-// registers; out-of-range offsets read zeros), four stages deep (38 KB each).
+// Operands. A is the quantized activation in its exact f16 form (written by
+// the quantizer next to the packed bytes: e2m1 * e4m3 per element, the
+// global scale left out), rows of pitch_h(K) bytes; every N-tile reads those
+// values as they are, with no conversion. B rows (one per weight column: the
+// weights in the byte-transposed layout, as the pages' GEMM consumed B
+// column-major) are K-packed FP4 with their E4M3 scales, in 16-row blocks
+// whose 64-element half steps are contiguous (512 bytes); they are converted
+// to f16 in registers (one scaled FP4 -> f16 conversion and one f16 multiply
+// per two elements). Tiles move from HBM to LDS by buffer loads that write
+// LDS directly (no staging registers; out-of-range offsets read zeros),
+// three stages of 64 K elements (42 KB each).
 //
-// LDS layout. A stage holds 256 A rows and 256 B rows of 64 bytes, unpadded;
-// the four 16-byte chunks of a row are XOR-swizzled with bits 2-3 of the row,
-// so that the 16 rows read by a 16-lane group of the fragment loads cover all
-// banks. Scales: 8 bytes per A row; per B row four dwords, one per pair of
-// scale groups (the packed weights store a pair of groups of four consecutive
-// K steps together, so a step's pairs are 2-byte pieces, and each is brought
-// in by a 2-byte load that fills a whole LDS dword, zero-extended).
+// LDS layout of a stage. A: 256 rows of 128 bytes (8 chunks of 16 bytes;
+// chunk c of row r stored at chunk c ^ ((r >> 1) & 7), so the 16 rows read by
+// a 16-lane group of fragment loads cover all banks). B: 256 rows of 32 bytes
+// (2 chunks, chunk c of row r at c ^ ((r >> 3) & 1)). B scales: per row two
+// dwords, one per pair of scale groups (the packed weights store a pair of
+// groups of four consecutive K steps together, so a half step's pairs are
+// 2-byte pieces; each is brought in by a 2-byte load that fills a whole LDS
+// dword, zero-extended).
 //
 // Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
 // 128 x 128 quadrant (4 x 4 tiles of 32 x 32 x 16). Lane l serves row / column
-// l % 32 and K half h = l / 32: in a 128-element step it holds elements
-// [64h, 64h + 64) (two 16-byte chunks), and substep s (0..7) feeds the MFMA
-// elements [64h + 8s, +8), inside scale group 4h + s / 2; A and B use the same
-// K permutation, so every k meets its own partner. The dequant of substep s + 1
-// is issued between the MFMAs of substep s.
+// l % 32 and K half h = l / 32: of a 64-element step it covers elements
+// [32h, 32h + 32), and substep s (0..3) feeds the MFMA elements [32h + 8s, +8),
+// inside scale group 2h + s / 2; A and B use the same K permutation, so every
+// k meets its own partner. A tile whose expert has fewer rows left runs a
+// variant with MI (1..3) instead of 4 row blocks of 32 per wave and loads only
+// its 64 * MI A rows.
 //
-// Grouped scheduling. Tiles come from a device-built list (expert, first
-// sorted row, row count); the grid is sized for the worst case and idle
-// work-groups leave at once, so the host never waits for routing counts.
-// Invalid rows and columns of a tile read a valid row instead (their results
-// are never stored). Rows are read in whole 128-element steps: the padding of
-// a partial last step is zero in both operands (the quantizers and the weight
-// prepack write it as zeros), so it adds nothing.
+// Scheduling. Work-group b runs on XCD b % 8 (the dispatcher deals work-groups
+// round-robin over the eight XCDs, each with its own L2), so b = 8 s + x
+// takes tile 8 (s / ntn) + x, N-tile s % ntn: all N-tiles of one tile run on
+// one XCD, at about the same time, and read its A rows through one L2. Tiles
+// come from a device-built list (expert, first sorted row, row count) with
+// all full tiles before the partial ones; the grid is sized for the worst
+// case and idle work-groups leave at once, so the host never waits for
+// routing counts. Invalid rows and columns of a tile read a valid row instead
+// (their results are never stored). Rows are read in whole steps: the padding
+// of a partial last step is zero in both operands (the quantizers and the
+// weight prepack write it as zeros), so it adds nothing.
 #include <type_traits>
 
 #include "common.hpp"
@@ -55,16 +64,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = kGemmBM;
 constexpr int BN = kGemmBN;
-constexpr int KB = 64;                 // packed bytes of K per step (128 elements)
-constexpr int NT = 256;                // threads per work-group
-constexpr int NSTAGE = 4;
-constexpr int A_BYTES = BM * KB;       // 16 KB
-constexpr int B_BYTES = BN * KB;
-constexpr int ASF_BYTES = BM * 8;      // 2 KB
-constexpr int BSF_BYTES = BN * 16;     // 4 KB: one dword per scale pair
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + ASF_BYTES + BSF_BYTES;
-constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;   // 152 KB
+constexpr int NT = 256;                 // threads per work-group
+constexpr int KS = 64;                  // K elements per step
+constexpr int NSTAGE = 3;
+constexpr int A_ROW = 2 * KS;           // bytes of one f16 A row per step
+constexpr int A_BYTES = BM * A_ROW;     // 32 KB
+constexpr int B_ROW = KS / 2;           // bytes of one packed B row per step
+constexpr int B_BYTES = BN * B_ROW;     // 8 KB
+constexpr int BSF_BYTES = BN * 8;       // 2 KB: two dwords per row
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES + BSF_BYTES;
+constexpr int kGuLd = 130;              // L1 epilogue: words per staged gate/up row
+constexpr int EPI_BYTES = BM * kGuLd * 4;
+constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES > EPI_BYTES ? NSTAGE * STAGE_BYTES : EPI_BYTES;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;        // raw buffer, 32-bit data format
+
+// s_waitcnt immediate: vmcnt (6 bits, split 4 + 2), expcnt left at 7, lgkmcnt
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 // Work-group barrier for the main loop. __syncthreads() (and any workgroup
 // fence, since the buffer-to-LDS loads count as LDS writes) first drains every
@@ -77,8 +92,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes;
@@ -94,11 +107,13 @@ void gemm_kernel(GemmParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int64_t K = p.K, N = p.N;
-    const int64_t ldq = pitch_q(K), ldsf = pitch_sf(K);      // padded row pitches (A)
-    const int64_t ldwsf = pitch_wsf(K);                       // packed weight scales
+    const int64_t ldq = pitch_q(K), lda = pitch_h(K);           // packed B row, f16 A row
+    const int64_t ldwsf = pitch_wsf(K);                         // packed weight scales
     const int ntn = (MODE == kGemmL1) ? (int)((p.I + 127) / 128) : (int)((N + BN - 1) / BN);
-    const int tile_idx = blockIdx.x / ntn;
-    const int nt = blockIdx.x - tile_idx * ntn;
+    const int xcd = blockIdx.x & 7;
+    const int slot = blockIdx.x >> 3;
+    const int tile_idx = 8 * (slot / ntn) + xcd;
+    const int nt = slot % ntn;
 
     int expert, row_start, row_count;
     if (MODE == kGemmDense) {
@@ -107,8 +122,9 @@ void gemm_kernel(GemmParams p) {
         row_count = (int)min((int64_t)BM, p.M - row_start);
         if (row_count <= 0) return;
     } else {
-        // both loads at once (tile_idx < max_tiles: the entry exists, and is
-        // used only when it is one of the num_tiles valid ones)
+        if (tile_idx >= p.max_tiles) return;      // the grid covers whole groups of 8 tiles
+        // both loads at once (the entry exists, and is used only when it is
+        // one of the num_tiles valid ones)
         const Tile t = p.tiles[tile_idx];
         const int ntiles = *p.num_tiles;
         // keeps the tile load above the branch (the compiler would sink it)
@@ -118,25 +134,26 @@ void gemm_kernel(GemmParams p) {
         row_start = t.row_start;
         row_count = t.row_count;
     }
-    // Each wave covers MI blocks of 32 rows, so a tile computes 64 * MI rows:
-    // the last tile of an expert usually holds fewer than 256 (at the prefill
-    // shape about 171 of 256 on average), and its MFMAs shrink with it. The
-    // loads still bring in all 256 rows (the extra ones repeat a valid row).
+    // Each wave covers MI blocks of 32 rows, so a tile computes and loads 64 *
+    // MI rows: the last tile of an expert usually holds fewer than 256 (at the
+    // prefill shape about 171 of 256 on average).
     const int mi_tile = __builtin_amdgcn_readfirstlane((row_count + 63) / 64);
     __shared__ uint32_t red[NT / 64];
     auto tile = [&](auto mi_c) {
         constexpr int MI = decltype(mi_c)::value;
-        // VALU per MFMA in the substeps' schedules: the dequant of one
-        // substep is about 11 VALU per operand (MI + 4 operands) spread over
-        // its 4 * MI MFMAs; the last substep's first kFirst MFMAs cover the
-        // fragment reads
-        constexpr int kValu = MI == 4 ? 5 : MI == 3 ? 6 : MI == 2 ? 8 : 14;
-        constexpr int kFirst = MI == 1 ? 2 : 6;
-        constexpr int kValuLast = MI == 4 ? 8 : MI == 3 ? 13 : MI == 2 ? 33 : 28;
+        constexpr int NA = 2 * MI;              // A loads per wave and stage (8 rows each)
+        constexpr int NL = NA + 4;              // all loads per wave and stage
+        constexpr int kWaitStage = waitcnt_imm(NL, 0);   // all but one stage's loads done
+        constexpr int kWaitAll = waitcnt_imm(0, 0);
+        // VALU per MFMA in the substeps' schedules: the B conversion of one
+        // substep is 32 VALU plus the scale pairs, over its 4 * MI MFMAs; the
+        // last substep's first kFirst MFMAs cover the fragment reads
+        constexpr int kValu = MI == 4 ? 3 : MI == 3 ? 3 : MI == 2 ? 4 : 8;
+        constexpr int kFirst = MI == 1 ? 2 : 4;
+        constexpr int kValuLast = MI == 4 ? 4 : MI == 3 ? 5 : MI == 2 ? 8 : 20;
 
         // ---- buffer resources and per-lane DMA offsets ---------------------------
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.aq, p.a_rows * ldq);
-        const __amdgpu_buffer_rsrc_t rasf = make_rsrc(p.asf, p.a_rows * ldsf);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ah, p.a_rows * lda);
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bq + (int64_t)expert * N * ldq, N * ldq);
         const __amdgpu_buffer_rsrc_t rbsf = make_rsrc(p.bsf + (int64_t)expert * N * ldwsf, N * ldwsf);
 
@@ -155,59 +172,32 @@ void gemm_kernel(GemmParams p) {
             const int64_t c = (int64_t)nt * BN + vc;
             return c < N ? c : 0;
         };
-        // data: wave w, instruction t (0..3) fills LDS slots (4w + t) * 64 + lane of
-        // 16 bytes: row (4w + t) * 16 + lane / 4, physical chunk lane & 3
-        uint32_t a_off[4], b_off[4];
+        // A: load u (0 .. 8 MI - 1) fills LDS bytes [1024 u, +1024) of the A
+        // region: rows 8u + lane / 8, physical chunk lane % 8. Wave w issues
+        // u = NA w + t.
+        // (fixed size: the host pass of the compiler drops the kernel when a
+        // nested lambda captures an array whose size depends on MI)
+        uint32_t a_off[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = (4 * wave + t) * 16 + (lane >> 2);
-            const int chunk = swz(row, lane & 3);
-            a_off[t] = (uint32_t)(a_src(row) * ldq + 16 * chunk);
-            b_off[t] = (uint32_t)(wq_row(b_src(row), ldq) + 16 * chunk);
+        for (int t = 0; t < NA; ++t) {
+            const int row = 8 * (NA * wave + t) + (lane >> 3);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+            a_off[t] = (uint32_t)(a_src(row) * lda + 16 * chunk);
         }
-        // A scales: wave w, instruction t (0..1) fills 4-byte slots (2w + t) * 64 +
-        // lane: row (2w + t) * 32 + lane / 2, bytes 4 * (lane & 1) .. +4 of the
-        // step's 8. B scales: instruction t (0..3) fills dword (4w + t) * 64 + lane
-        // with pair lane & 3 of row (4w + t) * 16 + lane / 4.
-        uint32_t asf_off[2], bsf_off[4];
+        // B: load v = 2w + t fills rows 32v + lane / 2, physical chunk lane % 2.
+        // B scales: load v = 2w + t fills dword 64v + lane = row (64v + lane) / 2,
+        // pair lane % 2 of the half step's two.
+        uint32_t b_off[2], bsf_off[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int row = (2 * wave + t) * 32 + (lane >> 1);
-            asf_off[t] = (uint32_t)(a_src(row) * ldsf + 4 * (lane & 1));
+            const int row = 32 * (2 * wave + t) + (lane >> 1);
+            const int chunk = (lane & 1) ^ ((row >> 3) & 1);
+            b_off[t] = (uint32_t)wq_off(b_src(row), ldq, 16 * chunk);
+            const int64_t n = b_src(row);
+            bsf_off[t] = (uint32_t)((n >> 4) * 16 * ldwsf + (n & 15) * 32 + (lane & 1) * 8);
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            bsf_off[t] = (uint32_t)wsf_off(b_src((4 * wave + t) * 16 + (lane >> 2)), ldwsf, 0, lane & 3);
 
-        const int nk = (int)(ldq / KB);
-        // part t (0..5) of the DMA of stage ks: t < 4 one A and one B data load,
-        // t = 4, 5 one A and two B scale loads
-        auto issue_part = [&](int ks, int t) {
-            uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-            // A rows advance by 64 bytes per step, packed weight blocks by 1 KB
-            const uint32_t kda = (uint32_t)ks * KB, kdb = (uint32_t)ks * kWqStep;
-            const uint32_t ksa = (uint32_t)ks * 8, ksb = (uint32_t)((ks >> 2) * kWsfQuad + (ks & 3) * 2);
-            if (t < 4) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(base + (4 * wave + t) * 1024),
-                                                         16, a_off[t], kda, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(base + A_BYTES + (4 * wave + t) * 1024),
-                                                         16, b_off[t], kdb, 0, 0);
-            } else {
-                const int u = t - 4;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rasf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + u) * 256), 4, asf_off[u], ksa, 0, 0);
-#pragma unroll
-                for (int v = 2 * u; v < 2 * u + 2; ++v)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rbsf, (lds_void*)(base + A_BYTES + B_BYTES + ASF_BYTES + (4 * wave + v) * 256), 2,
-                        bsf_off[v], ksb, 0, 0);
-            }
-        };
-        auto issue_stage = [&](int ks) {
-#pragma unroll
-            for (int t = 0; t < 6; ++t) issue_part(ks, t);
-        };
-
+        const int nk = (int)(ldq / 32);             // 64-element steps
         // ---- main loop ---------------------------------------------------------
         const int wm = wave >> 1, wn = wave & 1;
         const int l32 = lane & 31, h = lane >> 5;
@@ -220,139 +210,176 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        u32x4 fa[MI][2], fb[4][2];
-        uint32_t sa[MI];
-        u32x2 sb[4];      // B scale pairs 2h, 2h + 1: bytes 0-1 of each dword
         // Fragment rows are wm * 32 MI + 32 i + l32 (A) and wn * 128 + 32 j + l32
-        // (B): the 32 i / 32 j parts are multiples of 16, so the swizzle (bits
-        // 2-3 of the row) depends on the lane alone. Six per-lane offsets
-        // within a stage are formed once; per step each gets the stage base
-        // added once, and the fragments' row offsets are constants (the LDS
-        // reads' immediate offsets), instead of a full address per read.
-        const int sw = (l32 >> 2) & 3;
+        // (B): the 32 i / 32 j parts do not change the swizzles, which then
+        // depend on the lane alone. The per-lane offsets within a stage are
+        // formed once; the fragments' row offsets are the reads' immediates.
         const uint32_t a_row = (uint32_t)(wm * (32 * MI) + l32), b_row = (uint32_t)(wn * 128 + l32);
-        const uint32_t off_a0 = a_row * KB + 16 * ((2 * h) ^ sw);
-        const uint32_t off_a1 = a_row * KB + 16 * ((2 * h + 1) ^ sw);
-        const uint32_t off_b0 = A_BYTES + b_row * KB + 16 * ((2 * h) ^ sw);
-        const uint32_t off_b1 = A_BYTES + b_row * KB + 16 * ((2 * h + 1) ^ sw);
-        const uint32_t off_asf = A_BYTES + B_BYTES + a_row * 8 + 4 * h;
-        const uint32_t off_bsf = A_BYTES + B_BYTES + ASF_BYTES + b_row * 16 + 8 * h;
-        auto read_frags = [&](int ks) {
-            const uint8_t* base = smem_raw + (ks % NSTAGE) * STAGE_BYTES;
-            const uint8_t* pa0 = base + off_a0;
-            const uint8_t* pa1 = base + off_a1;
-            const uint8_t* pb0 = base + off_b0;
-            const uint8_t* pb1 = base + off_b1;
-            const uint8_t* pas = base + off_asf;
-            const uint8_t* pbs = base + off_bsf;
+        const int sw_a = (l32 >> 1) & 7;
+        uint32_t off_a[4];
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                fa[i][0] = *reinterpret_cast<const u32x4*>(pa0 + i * 32 * KB);
-                fa[i][1] = *reinterpret_cast<const u32x4*>(pa1 + i * 32 * KB);
-                sa[i] = *reinterpret_cast<const uint32_t*>(pas + i * 32 * 8);
-            }
+        for (int s = 0; s < 4; ++s) off_a[s] = a_row * A_ROW + 16 * ((4 * h + s) ^ sw_a);
+        const uint32_t off_b = A_BYTES + b_row * B_ROW + 16 * (h ^ ((l32 >> 3) & 1));
+        const uint32_t off_bsf = A_BYTES + B_BYTES + b_row * 8 + 4 * h;
+
+        half8_t fa[2][MI];      // A operands of substep s in fa[s & 1]
+        u32x4 fb[4];            // packed B of the step: dword s = substep s
+        uint32_t sb[4];         // B scale pair of the step (2 bytes)
+        half8_t hb[2][4];       // converted B operands of substep s in hb[s & 1]
+        half2_t spb[4];         // scale pairs of the current group of two substeps
+        auto read_a = [&](int st, int s, half8_t (&dst)[MI]) {
+            const uint8_t* pa = smem_raw + st * STAGE_BYTES + off_a[s];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) dst[i] = *reinterpret_cast<const half8_t*>(pa + i * 32 * A_ROW);
+        };
+        auto read_b = [&](int st) {
+            const uint8_t* base = smem_raw + st * STAGE_BYTES;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                fb[j][0] = *reinterpret_cast<const u32x4*>(pb0 + j * 32 * KB);
-                fb[j][1] = *reinterpret_cast<const u32x4*>(pb1 + j * 32 * KB);
-                // pairs 2h and 2h + 1, each in the low half of its dword (the
-                // dequant picks the byte from either, no joining needed)
-                sb[j] = *reinterpret_cast<const u32x2*>(pbs + j * 32 * 16);
+                fb[j] = *reinterpret_cast<const u32x4*>(base + off_b + j * 32 * B_ROW);
+                sb[j] = *reinterpret_cast<const uint32_t*>(base + off_bsf + j * 32 * 8);
             }
         };
-        // operands of substep s in registers s & 1
-        half8_t ha[2][MI], hb[2][4];
-        // scale pairs of the current group of two substeps (one scale group):
-        // formed on even substeps, reused on the odd ones (also across the
-        // step boundary: substep 0 is dequantized at the end of the previous
-        // step)
-        half2_t spa[MI], spb[4];
-        auto deq = [&](int s, half8_t (&xa)[MI], half8_t (&xb)[4]) {
+        auto deq_b = [&](int s, half8_t (&dst)[4]) {
             if ((s & 1) == 0) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i) spa[i] = scale_pair((sa[i] >> (8 * (s >> 1))) & 0xFFu);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j][s >> 2] >> (8 * ((s >> 1) & 1))) & 0xFFu);
+                for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu);
             }
 #pragma unroll
-            for (int i = 0; i < MI; ++i) xa[i] = dequant8(fa[i][s >> 2][s & 3], spa[i]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xb[j] = dequant8(fb[j][s >> 2][s & 3], spb[j]);
+            for (int j = 0; j < 4; ++j) dst[j] = dequant8(fb[j][s], spb[j]);
         };
 
-        // Pipeline: stages ks+1..ks+3 are in flight while step ks computes. Every
-        // substep s issues its 16 MFMAs with the dequant of substep s + 1 between
-        // them. Substep 7 starts with the wait for this wave's DMA of stage ks+1
-        // and the barrier (the other waves' DMA of it is then visible, and buffer
-        // (ks-1) % 4, which the next step refills, has been read by everyone),
-        // reads the fragments of step ks+1, and dequantizes substep 0 of step ks+1
-        // between its later MFMAs, so that no dequant runs outside an MFMA shadow.
-        // Scheduling barriers keep each substep's instructions together.
-        for (int s0 = 0; s0 < NSTAGE - 1 && s0 < nk; ++s0) issue_stage(s0);
-        // only stage 0 is needed now: wait until the later stages' loads are
-        // all that is outstanding (14 per stage), not for all of them
-        if (nk >= 3) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
-        else if (nk == 2) __builtin_amdgcn_s_waitcnt(0x007E);   // vmcnt(14) lgkmcnt(0)
-        else __builtin_amdgcn_s_waitcnt(0x0070);                // vmcnt(0) lgkmcnt(0)
-        lds_barrier();
-        read_frags(0);
-        deq(0, ha[0], hb[0]);
+        // load j (0..3) of part t of the DMA of stage ks (none when that part
+        // has fewer loads): part t < 2 holds A loads t MI .. t MI + MI - 1,
+        // part 2 the two B loads and the two scale loads
+        auto issue_one = [&](int ks, int st, int t, int j) {
+            uint8_t* base = smem_raw + st * STAGE_BYTES;
+            if (t < 2) {
+                if (j < MI)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        ra, (lds_void*)(base + (NA * wave + t * MI + j) * 1024), 16, a_off[t * MI + j],
+                        (uint32_t)ks * A_ROW, 0, 0);
+            } else if (j < 2) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_void*)(base + A_BYTES + (2 * wave + j) * 1024), 16, b_off[j],
+                    (uint32_t)ks * kWqHalf, 0, 0);
+            } else {
+                // half step ks of K step kst = ks / 2: pairs 2 (ks % 2) + {0, 1}
+                const int kst = ks >> 1;
+                const uint32_t ksb = (uint32_t)((kst >> 2) * kWsfQuad + (kst & 3) * 2 + (ks & 1) * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rbsf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + j - 2) * 256), 2, bsf_off[j - 2],
+                    ksb, 0, 0);
+            }
+        };
 
-        // One K step. Phase 0: steady state (refill a stage, wait until 28 loads
-        // remain, fetch the next step); 1 and 2: the last two refills have been
-        // issued (wait until 14 / 0 remain); 3: the last step. Every condition is a
-        // compile-time constant, so a step is one basic block the scheduler can
-        // interleave freely.
-        auto step = [&](int ks, auto mode_c) {
+        auto issue_stage = [&](int ks, int st) {
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) issue_one(ks, st, t, j);
+        };
+
+        // One K step in four substeps. Substeps 0..2 run as four chunks, one
+        // per B column block j: its MI MFMAs, the conversion of its operand of
+        // the next substep, and one load of the refill of stage ks+2 (the
+        // loads, issued back to back, stall the wave's instruction stream).
+        // Substep 3 starts with the wait for this wave's DMA of stage ks+1 and
+        // the barrier (the other waves' DMA of it is then visible, and the
+        // buffer the refills of step ks+1 overwrite has been read by
+        // everyone), reads the B fragments and the first A fragments of step
+        // ks+1, and converts its first B operands between the later MFMAs.
+        // Phase 0: steady state (refill, wait until NL loads remain); 1: the
+        // last refill has been issued (wait until none remain); 2: the last
+        // step. Every condition is a compile-time constant, so a step is one
+        // basic block.
+        auto step = [&](int ks, auto mode_c, int st) {
             constexpr int PH = decltype(mode_c)::value;
+            const int sn = st == NSTAGE - 1 ? 0 : st + 1;          // stage of ks + 1
+            const int sr = st == 0 ? NSTAGE - 1 : st - 1;          // stage of ks + 2
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                // the refill of stage ks+3 is spread over substeps 0..5: a burst of
-                // fourteen LDS-DMA issues at once stalls the MFMA stream
-                if (PH == 0 && s < 6) issue_part(ks + NSTAGE - 1, s);
-                if (s < 7) {
-                    deq(s + 1, ha[(s + 1) & 1], hb[(s + 1) & 1]);
-                } else if (PH < 3) {
-                    // this wave's DMA of stage ks+1 is done when at most the stages
-                    // issued after it are outstanding; lgkmcnt(0): its own fragment
-                    // reads of this step are complete before it passes the barrier
-                    if (PH == 0) __builtin_amdgcn_s_waitcnt(0x407C);        // vmcnt(28) lgkmcnt(0)
-                    if (PH == 1) __builtin_amdgcn_s_waitcnt(0x007E);        // vmcnt(14) lgkmcnt(0)
-                    if (PH == 2) __builtin_amdgcn_s_waitcnt(0x0070);        // vmcnt(0) lgkmcnt(0)
-                    lds_barrier();
-                    read_frags(ks + 1);
-                }
+            for (int s = 0; s < 3; ++s) {
+                read_a(st, s + 1, fa[(s + 1) & 1]);
+                if (s == 1) {
 #pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ha[s & 1][i], hb[s & 1][j],
-                                                                            acc[i][j], 0, 0, 0);
-                if (s < 7) {
-#pragma unroll
-                    for (int k = 0; k < 4 * MI; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);   // its VALU share
-                    }
-                } else if (PH < 3) {
-                    deq(0, ha[0], hb[0]);
-                    // the fragment reads land under the first MFMAs
-                    __builtin_amdgcn_sched_group_barrier(0x100, 3 * MI + 12, 0);  // the LDS reads
-                    __builtin_amdgcn_sched_group_barrier(0x008, kFirst, 0);
-#pragma unroll
-                    for (int k = 0; k < 4 * MI - kFirst; ++k) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, kValuLast, 0);
-                    }
+                    for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j] >> 8) & 0xFFu);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                    for (int i = 0; i < MI; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][i], hb[s & 1][j],
+                                                                            acc[i][j], 0, 0, 0);
+                    hb[(s + 1) & 1][j] = dequant8(fb[j][s + 1], spb[j]);
+                    if (PH == 0) issue_one(ks + NSTAGE - 1, sr, s, j);
+#pragma unroll
+                    for (int i = 0; i < MI; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);    // its VALU share
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
+            if (PH < 2) {
+                // this wave's DMA of stage ks+1 is done when at most the loads
+                // issued after it are outstanding; lgkmcnt(0): its own fragment
+                // reads of this step are complete before it passes the barrier
+                if (PH == 0) __builtin_amdgcn_s_waitcnt(kWaitStage);
+                if (PH == 1) __builtin_amdgcn_s_waitcnt(kWaitAll);
+                lds_barrier();
+                read_b(sn);
+                read_a(sn, 0, fa[0]);
+            }
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1][i], hb[1][j], acc[i][j], 0, 0, 0);
+            if (PH < 2) {
+                deq_b(0, hb[0]);
+                // the fragment reads land under the first MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, MI + 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, kFirst, 0);
+#pragma unroll
+                for (int k = 0; k < 4 * MI - kFirst; ++k) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, kValuLast, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         };
+        // Pipeline: stages ks+1 and ks+2 are in flight while step ks computes;
+        // the refill of stage ks+2 goes into the buffer step ks-1 used, which
+        // every wave has finished reading at the barrier before step ks.
+        issue_stage(0, 0);
+        if (nk > 1) issue_stage(1, 1);
+        // only stage 0 is needed now: wait until stage 1's loads are all that
+        // is outstanding
+        if (nk > 1) __builtin_amdgcn_s_waitcnt(kWaitStage);
+        else __builtin_amdgcn_s_waitcnt(kWaitAll);
+        lds_barrier();
+        read_b(0);
+        read_a(0, 0, fa[0]);
+        deq_b(0, hb[0]);
+
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using P2 = std::integral_constant<int, 2>;
+        // steady state, NSTAGE steps per iteration (constant stage buffers);
+        // then the remaining steps with the buffer computed at run time
         int ks = 0;
-        for (; ks + NSTAGE - 1 < nk; ++ks) step(ks, std::integral_constant<int, 0>{});
-        if (nk - ks == 3) step(ks++, std::integral_constant<int, 1>{});
-        if (nk - ks == 2) step(ks++, std::integral_constant<int, 2>{});
-        step(ks, std::integral_constant<int, 3>{});
+        for (; ks + NSTAGE + 1 < nk; ks += NSTAGE) {
+            step(ks, P0{}, 0);
+            step(ks + 1, P0{}, 1);
+            step(ks + 2, P0{}, 2);
+        }
+        for (; ks + NSTAGE - 1 < nk; ++ks) step(ks, P0{}, ks % NSTAGE);
+        if (ks + 1 < nk) {
+            step(ks, P1{}, ks % NSTAGE);
+            ++ks;
+        }
+        step(ks, P2{}, ks % NSTAGE);
         __syncthreads();
 
         // ---- epilogue ------------------------------------------------------------
@@ -368,7 +395,7 @@ void gemm_kernel(GemmParams p) {
             // padded to 130 words (the two lane halves' rows, four apart, then
             // fall in different banks; 8-byte reads stay aligned); then all
             // threads apply SiLU and store act row by row (coalesced).
-            constexpr int GU_LD = 130;
+            constexpr int GU_LD = kGuLd;
             static_assert(64 * MI * GU_LD * 4 <= LDS_BYTES, "gate/up staging fits in LDS");
             uint32_t* gu = reinterpret_cast<uint32_t*>(smem_raw);     // [64 MI][GU_LD] g | u << 16
             uint32_t amax_bits = 0;
@@ -550,7 +577,7 @@ template <int MODE>
 hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     const int64_t ntn = (MODE == kGemmL1) ? (p.I + 127) / 128 : (p.N + BN - 1) / BN;
     const int64_t mt = (MODE == kGemmDense) ? (p.M + BM - 1) / BM : p.max_tiles;
-    const int64_t grid = mt * ntn;
+    const int64_t grid = (mt + 7) / 8 * 8 * ntn;     // whole groups of 8 tiles (one per XCD)
     if (grid <= 0) return hipSuccess;
     static std::atomic<int> lds_set[kMaxDevices];
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<MODE>), LDS_BYTES, lds_set);
@@ -563,7 +590,7 @@ hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     // 32-bit buffer offsets: every operand must stay below 2 GiB
-    if (p.a_rows * pitch_q(p.K) >= 0x7FFFFFFF || p.N * pitch_q(p.K) >= 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (p.a_rows * pitch_h(p.K) >= 0x7FFFFFFF || p.N * pitch_q(p.K) >= 0x7FFFFFFF) return hipErrorInvalidValue;
     switch (p.mode) {
         case kGemmDense: return launch_mode<kGemmDense>(p, s);
         case kGemmL1: return launch_mode<kGemmL1>(p, s);

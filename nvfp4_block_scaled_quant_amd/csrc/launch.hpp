@@ -53,32 +53,46 @@ hipError_t launch_amax_bf16(const uint16_t* x, int64_t n, uint32_t* slot, hipStr
 hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, uint32_t* slots,
                                     hipStream_t s);
 
+// Row pitches of the GEMM operand layout: packed data padded to whole
+// 128-element K steps, scales to whole 8-byte steps; the exact f16 form of a
+// quantized activation (e2m1 * e4m3 per element, the global scale left out)
+// has the same padded length, 2 bytes per element.
+__host__ __device__ inline int64_t pitch_q(int64_t K) { return (K / 2 + 63) / 64 * 64; }
+__host__ __device__ inline int64_t pitch_sf(int64_t K) { return (K / 16 + 7) / 8 * 8; }
+__host__ __device__ inline int64_t pitch_h(int64_t K) { return 4 * pitch_q(K); }
+
 // Row-block quantization of x (M, K) with amax taken from *amax_slot, or with
 // the global scale *gs_in when gs_in is not null. Rows at or beyond *m_dev
 // (when m_dev is not null) are left untouched. gs_out receives gs.
-// Output rows are ldq bytes (q) and ldsf bytes (sf) apart.
+// Output rows are ldq bytes (q) and ldsf bytes (sf) apart; when h is not null
+// the dequantized f16 values (without gs) go to rows of pitch_h(K) bytes too.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
                              const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
                              int64_t ldsf, float* gs_out, hipStream_t s,
-                             const float* gs_in = nullptr);
+                             const float* gs_in = nullptr, uint16_t* h = nullptr);
 
-// Row pitches of the GEMM operand layout: packed data padded to whole
-// 128-element K steps, scales to whole 8-byte steps.
-__host__ __device__ inline int64_t pitch_q(int64_t K) { return (K / 2 + 63) / 64 * 64; }
-__host__ __device__ inline int64_t pitch_sf(int64_t K) { return (K / 16 + 7) / 8 * 8; }
+// Quantized rows (M, K/2) + (M, K/16), K % 16 == 0, unpadded -> their exact
+// f16 values in rows of pitch_h(K) bytes, zero padded.
+hipError_t launch_dequant_rows_f16(const uint8_t* q, const uint8_t* sf, int64_t M, int64_t K,
+                                   uint16_t* h, hipStream_t s);
 
 // Packed weight layout. A weight matrix is N rows (one per output column) of
 // pitch_q(K) bytes, K-packed; rows are grouped in blocks of 16, and inside a
-// block the 64 bytes of one 128-element K step of all 16 rows are stored
-// together (1 KB), step after step. So one K step of a 16-row block, the unit
-// an MFMA operand load covers, is contiguous.
+// block the 32 bytes of one 64-element half of a K step of all 16 rows are
+// stored together (512 bytes), half step after half step. So one half step of
+// a 16-row block, the unit a GEMM stage holds, is contiguous, and so is one
+// whole 128-element K step (1 KB, the unit a streaming load covers).
 // Scales: per block, groups of four K steps (512 bytes): row c (0..15), pair q
 // (0..3: groups 2q, 2q+1 of a step), step u of the four, then the two bytes.
 // The two scale bytes a streaming lane needs for four consecutive steps are
 // thus one 8-byte piece, and a wave reads 512 contiguous bytes at once.
 constexpr int kWqStep = 16 * 64;      // bytes of one K step of a 16-row block
+constexpr int kWqHalf = 16 * 32;      // bytes of one half step of a 16-row block
 constexpr int kWsfQuad = 16 * 32;     // scale bytes of four K steps of a block
-__host__ __device__ inline int64_t wq_row(int64_t n, int64_t ldq) { return (n >> 4) * 16 * ldq + (n & 15) * 64; }
+// offset of byte kh (0..pitch_q - 1) of packed row n
+__host__ __device__ inline int64_t wq_off(int64_t n, int64_t ldq, int64_t kh) {
+    return (n >> 4) * 16 * ldq + (kh >> 5) * kWqHalf + (n & 15) * 32 + (kh & 31);
+}
 // scale row pitch of the packed weights: whole groups of four K steps
 __host__ __device__ inline int64_t pitch_wsf(int64_t K) { return (pitch_q(K) / 64 + 3) / 4 * 32; }
 // offset of scale pair q of K step st of row n (two bytes: groups 8st + 2q, +1)
@@ -119,6 +133,7 @@ struct SmallQuant {
     uint8_t* sf;
     int64_t ldsf;
     float* gs;
+    uint16_t* h;             // exact f16 values, rows of pitch_h(K) bytes, or null
 };
 constexpr int64_t kSmallQuantMax = 1 << 17;   // elements: larger inputs take the two-kernel path
 
@@ -145,8 +160,11 @@ enum GemmMode { kGemmDense = 0, kGemmL1 = 1, kGemmL2 = 2 };
 struct GemmParams {
     int mode;
     // A: rows of quantized activations, pitches pitch_q(K) / pitch_sf(K)
+    // (weight-streaming kernel), or their exact f16 values, pitch pitch_h(K)
+    // (tiled kernel)
     const uint8_t* aq;
     const uint8_t* asf;
+    const uint16_t* ah;
     int64_t M;                 // dense: rows of A
     int64_t a_rows;            // rows in the A tensor (bounds of the buffer loads)
     const int32_t* a_gather;   // L1: sorted row -> slot index; token = slot / topk

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
 __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, const int32_t* __restrict__ m_dev,
     const uint32_t* __restrict__ amax_slot, const float* __restrict__ gs_in, uint8_t* __restrict__ q,
-    int64_t ldq, uint8_t* __restrict__ sf, int64_t ldsf, float* __restrict__ gs_out) {
+    int64_t ldq, uint8_t* __restrict__ sf, int64_t ldsf, float* __restrict__ gs_out,
+    uint8_t* __restrict__ h) {
     const QuantScales qs = gs_in ? scales_from_gs(*gs_in) : make_scales(__uint_as_float(*amax_slot));
     if (gs_out && blockIdx.x == 0 && threadIdx.x == 0) *gs_out = qs.gs;
     const int64_t rows = m_dev ? min((int64_t)(*m_dev), M) : M;
@@ -93,14 +94,33 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kRowBlocks; ++u)
-            quantize_row_block_loaded(v[u][0], v[u][1], b + u * step, groups, qs, q, ldq, sf, ldsf);
+            quantize_row_block_loaded(v[u][0], v[u][1], b + u * step, groups, qs, q, ldq, sf, ldsf, h);
     }
-    for (; b < nblocks; b += step) quantize_row_block(x, b, groups, qs, q, ldq, sf, ldsf);
+    for (; b < nblocks; b += step) quantize_row_block(x, b, groups, qs, q, ldq, sf, ldsf, h);
+}
+
+// One thread per 16-element block of quantized rows (M, K/2) + (M, K/16):
+// its exact f16 values into rows of pitch_h(K) bytes; the thread of a row's
+// last block also zeroes the row's padding.
+__global__ __launch_bounds__(kThreads) void dequant_rows_f16_kernel(const uint8_t* __restrict__ q,
+                                                                    const uint8_t* __restrict__ sf,
+                                                                    int64_t M, int64_t K,
+                                                                    uint8_t* __restrict__ h) {
+    const int64_t groups = K / 16, ldh = pitch_h(K);
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < M * groups;
+         b += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = b / groups, g = b - r * groups;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(q + b * 8);
+        store_block_f16(h + r * ldh + g * 32, w[0], w[1], sf[b]);
+        if (g == groups - 1)
+            for (int64_t j = groups * 32; j < ldh; j += 16)
+                *reinterpret_cast<u32x4*>(h + r * ldh + j) = (u32x4){0u, 0u, 0u, 0u};
+    }
 }
 
 // Canonical (R, C) byte matrices -> the packed weight layout (launch.hpp),
 // through a 64 x 64 LDS tile: reads along C are coalesced, writes land in
-// 64-byte runs (data) or 2-byte pieces (scales).
+// 32-byte runs (data) or 2-byte pieces (scales).
 __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
     const uint8_t* __restrict__ in, int64_t R, int64_t C, uint8_t* __restrict__ out, int64_t ldo,
     int scale_layout) {
@@ -120,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void pack_weights_kernel(
         const int64_t r = r0 + rr, c = c0 + cc;
         if (c < C && r < ldo) {
             const int64_t o = scale_layout ? wsf_off(c, ldo, r >> 3, (int)((r & 7) >> 1)) + (r & 1)
-                                           : (c >> 4) * 16 * ldo + (r >> 6) * kWqStep + (c & 15) * 64 + (r & 63);
+                                           : wq_off(c, ldo, r);
             dst[o] = tile[rr][cc];
         }
     }
@@ -217,9 +237,19 @@ hipError_t launch_amax_bf16_batched(const uint16_t* x, int64_t E, int64_t per, u
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, const int32_t* m_dev,
                              const uint32_t* amax_slot, uint8_t* q, int64_t ldq, uint8_t* sf,
-                             int64_t ldsf, float* gs_out, hipStream_t s, const float* gs_in) {
+                             int64_t ldsf, float* gs_out, hipStream_t s, const float* gs_in,
+                             uint16_t* h) {
     const int g = grid_for((M * (K / 16) + kRowBlocks - 1) / kRowBlocks, 1 << 20);
-    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, gs_in, q, ldq, sf, ldsf, gs_out);
+    quant_rows_kernel<<<g, kThreads, 0, s>>>(x, M, K, m_dev, amax_slot, gs_in, q, ldq, sf, ldsf, gs_out,
+                                             reinterpret_cast<uint8_t*>(h));
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_rows_f16(const uint8_t* q, const uint8_t* sf, int64_t M, int64_t K,
+                                   uint16_t* h, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const int g = grid_for(M * (K / 16), 1 << 16);
+    dequant_rows_f16_kernel<<<g, kThreads, 0, s>>>(q, sf, M, K, reinterpret_cast<uint8_t*>(h));
     return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const int64_t groups = xq.K / 16;
         for (int64_t b = (int64_t)(blockIdx.x - 1) * kRouteThreads + tid; b < xq.M * groups;
              b += (int64_t)(gridDim.x - 1) * kRouteThreads)
-            quantize_row_block(xq.x, b, groups, qs, xq.q, xq.ldq, xq.sf, xq.ldsf);
+            quantize_row_block(xq.x, b, groups, qs, xq.q, xq.ldq, xq.sf, xq.ldsf,
+                               reinterpret_cast<uint8_t*>(xq.h));
         return;
     }
     extern __shared__ int32_t lds[];

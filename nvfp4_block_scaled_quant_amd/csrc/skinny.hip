@@ -17,7 +17,8 @@
 //   8 weight rows: column c of the 8 MFMA column blocks f (block f
 //   holds weight rows 16f + c of the wave's 128). In the packed weight layout
 //   one such load instruction (16 rows x 64 bytes of one K step of a 16-row
-//   block) reads one contiguous kilobyte.
+//   block, stored as two half steps of 16 x 32 bytes) reads one contiguous
+//   kilobyte.
 //   Dword s of a load is the B operand of v_mfma_f32_16x16x32_f16 for
 //   substep s (K values 32q + 8s .. +8 of the step); A rows are read from LDS
 //   with the same K permutation, so every k meets its own partner. Nothing of
@@ -107,7 +108,7 @@ void skinny_kernel(GemmParams p) {
             ok[f] = row < N;
             row = ok[f] ? row : 0;
         }
-        boff[f] = (uint32_t)(wq_row(row, ldq) + 16 * q);
+        boff[f] = (uint32_t)wq_off(row, ldq, 16 * q);       // bytes [16q, 16q + 16) of step 0
         sfoff[f] = (uint32_t)wsf_off(row, ldwsf, 0, q);
     }
     // a wave whose columns all lie beyond the matrix streams nothing

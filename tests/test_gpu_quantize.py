@@ -123,9 +123,9 @@ def _padded_rows(a, pitch):
 
 
 def _packed_data(q, ldq):
-    # 16-row blocks whose 64-byte K steps are stored together
+    # 16-row blocks whose 32-byte half steps are stored together
     E, _, C = q.shape
-    return _padded_rows(q, ldq).reshape(E, C // 16, 16, ldq // 64, 64).transpose(0, 1, 3, 2, 4)
+    return _padded_rows(q, ldq).reshape(E, C // 16, 16, ldq // 32, 32).transpose(0, 1, 3, 2, 4)
 
 
 def _packed_scales(sf, ldwsf):
@@ -147,7 +147,7 @@ def test_prepack_weights_layout(nv, E, K, N):
     sf = rng.integers(0, 256, (E, K // 16, N)).astype(np.uint8)
     q_t, sf_t = (to_host(t) for t in nv.prepack_weights(to_dev(q), to_dev(sf)))
     ldq, _, ldwsf = nv.operand_pitches(K)
-    assert q_t.shape == (E, N // 16, ldq // 64, 16, 64)
+    assert q_t.shape == (E, N // 16, ldq // 32, 16, 32)
     assert sf_t.shape == (E, N // 16, ldwsf // 32, 16, 32)
     assert (q_t == _packed_data(q, ldq)).all()
     assert (sf_t == _packed_scales(sf, ldwsf)).all()

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(nv):
 
 
 def test_strerror_and_version(nv):
-    assert nv.version() == (4, 1)
+    assert nv.version() == (5, 0)
     for code in range(7):
         assert len(nv.strerror(code)) > 0
     assert nv.strerror(99) == "unknown status"
@@ -84,17 +84,30 @@ def test_quantize_weights_argument_errors(nv):
 
 def test_gemm_argument_errors(nv):
     f = lib(nv).nvfp4_gemm
+    ws = lib(nv).nvfp4_gemm_workspace
     args = [p(A16)] * 6
-    assert f(*args, 4, 16, 24, p(A16), None) == 2       # K % 16
-    assert f(*args, 4, 16, 64, p(A16), None) == 2       # K % 128
-    assert f(*args, 4, 24, 128, p(A16), None) == 2      # N % 16
-    assert f(*args, -4, 16, 128, p(A16), None) == 1
-    assert f(*args, 0, 16, 128, p(A16), None) == 0      # M == 0: nothing to do
+    big = 1 << 40
+
+    def call(a, M, N, K, wsp=A16, nbytes=big):
+        return f(*a, M, N, K, p(A16), p(wsp), nbytes, None)
+
+    assert call(args, 4, 16, 24) == 2                   # K % 16
+    assert call(args, 4, 24, 128) == 2                  # N % 16
+    assert call(args, -4, 16, 128) == 1
+    assert call(args, 0, 16, 128) == 0                  # M == 0: nothing to do
     bad = [p(A16)] * 5 + [p(0)]
-    assert f(*bad, 4, 16, 128, p(A16), None) == 1
+    assert call(bad, 4, 16, 128) == 1
     mis = [p(A16)] * 3 + [p(A16 + 8)] + [p(A16)] * 2   # bq not 16-byte aligned
-    assert f(*mis, 4, 16, 128, p(A16), None) == 1
-    assert f(*args, 1 << 20, 16, 1 << 13, p(A16), None) == 2   # A beyond 32-bit offsets
+    assert call(mis, 4, 16, 128) == 1
+    assert call(args, 1 << 20, 16, 1 << 13) == 2        # A beyond 32-bit offsets
+    # the workspace holds A as f16, rows padded to whole 128-element steps
+    assert ws(4, 16, 144) == 4 * 512                    # K = 144 pads to 256 elements: 512 bytes a row
+    assert ws(3, 16, 16) == 3 * 256                      # K = 16: one 128-element step, 256 bytes a row
+    assert ws(256, 6144, 7168) == 256 * 7168 * 2
+    assert ws(4, 16, 24) == 0 and ws(-1, 16, 128) == 0
+    assert call(args, 4, 16, 144, nbytes=ws(4, 16, 144) - 1) == 3
+    assert call(args, 4, 16, 144, wsp=A16 + 64) == 3    # misaligned workspace
+    assert call(args, 4, 16, 144, wsp=0) == 3
 
 
 def test_operand_pitches(nv):
