@@ -12,9 +12,11 @@ HBM before the timed region starts.
 
 The JSON line reports tokens/s (value), effective TFLOP/s (6 * slots * H * I per
 step), per-stage device times from HIP events recorded by the library on its
-stream, the L1 GEMM's MFMA roofline fraction, a decode-batch measurement (8
-tokens, weight HBM GB/s) and the CPU oracle timed on a bounded sample of the
-prefill workload on this host's cores.
+stream, the L1 and L2 GEMMs' MFMA roofline fractions, and beside them the other
+configurations of the recipe: the skewed prefill batch (8192 tokens), the dense
+single-expert GEMM (256 x 7168 x 6144), the decode batch (8 tokens, weight HBM
+GB/s, cycling through eight seeded routings), and the CPU oracle timed on the
+whole prefill workload on this host's cores.
 """
 import argparse
 import hashlib
@@ -93,8 +95,13 @@ def make_weights(nv, cfg):
     return w13, w13sf, w13a, w2, w2sf, w2a
 
 
-def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=None):
-    """Run warmup + timed steps; return (ms per step, per-stage ms, S_valid).
+def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=None, routings=1):
+    """Run warmup + timed steps; return (ms per step, per-stage ms, S_valid,
+    the ids of every routing used, whether y is finite).
+
+    routings: how many seeded routings (logit draws of the config's recipe
+    with seeds seed_x, seed_x + 1, ...) the steps cycle through, so that a
+    small batch does not touch the same experts in every step.
 
     variant: None (the layer as specified), "static_x" (nvfp4_moe_forward_ex
     with a static gs1, set to the value the dynamic rule gives for this x, so
@@ -109,10 +116,12 @@ def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=Non
     import numpy as np
     import torch
     import workloads as W
+    import dataclasses
     x = to_dev(W.activations(cfg))
-    ids_np, wts_np = W.routing(cfg)
-    ids, wts = to_dev(ids_np), to_dev(wts_np)
-    s_valid = int(((ids_np >= 0) & (ids_np < cfg.E)).sum())
+    routes = [W.routing(dataclasses.replace(cfg, seed_x=cfg.seed_x + r)) for r in range(routings)]
+    ids_np = np.stack([r[0] for r in routes])
+    dev_routes = [(to_dev(i), to_dev(w)) for i, w in routes]
+    s_valid = int(((ids_np[0] >= 0) & (ids_np[0] < cfg.E)).sum())
     ws = torch.empty((nv.moe_workspace_size(cfg.T, cfg.H, cfg.I, cfg.E, cfg.topk),),
                      dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
@@ -123,22 +132,23 @@ def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=Non
         w13, w13sf, w13a, w2, w2sf, w2a = weights
         weights = (w13, w13sf, torch.stack([w13a, w13a], dim=1).contiguous(), w2, w2sf, w2a)
 
-    def step(ev=None):
+    def step(i, ev=None):
+        ids, wts = dev_routes[i % routings]
         nv.moe_forward(x, ids, wts, *weights, y=y, workspace=ws, stage_events=ev, x_gs=x_gs)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
     events = [nv.StageEvents() for _ in range(steps if events_in_loop else min(steps, 10))]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i] if events_in_loop else None)
+        step(i, events[i] if events_in_loop else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     if not events_in_loop:
-        for ev in events:
-            step(ev)
+        for i, ev in enumerate(events):
+            step(i, ev)
         torch.cuda.synchronize()
     per = [ev.elapsed_ms() for ev in events]
     stage_ms = {k: float(np.mean([p[k] for p in per])) for k in per[0]}
@@ -169,15 +179,88 @@ def time_router(nv, cfg, launches=200):
 
 
 def decode_bytes(cfg, ids_np):
-    """Algorithmic HBM bytes of one decode step: every touched expert's w13 and
-    w2 bytes and scales, plus x, y, the routing arrays and the intermediates."""
+    """Algorithmic HBM bytes of one decode step, averaged over the routings in
+    ids_np (R, T, topk): every touched expert's w13 and w2 bytes and scales,
+    plus x, y, the routing arrays and the intermediates. Returns (bytes, mean
+    number of touched experts)."""
     import numpy as np
     H, I, E = cfg.H, cfg.I, cfg.E
     per_expert = (H // 2) * 2 * I + (H // 16) * 2 * I + (I // 2) * H + (I // 16) * H
-    touched = len(np.unique(ids_np[(ids_np >= 0) & (ids_np < E)]))
+    touched = float(np.mean([len(np.unique(r[(r >= 0) & (r < E)])) for r in ids_np]))
     S = cfg.T * cfg.topk
     act = S * I * 2 * 2 + S * (I // 2 + I // 16) * 2 + S * H * 4 * 2
     return touched * per_expert + cfg.T * H * 2 * 2 + act, touched
+
+
+def time_decode(nv, weights, steps, routings=8):
+    """The decode batch (8 tokens, top-8 of 48) cycling through `routings`
+    seeded routings, so that consecutive steps touch different expert sets;
+    bytes are the routings' mean algorithmic weight bytes."""
+    import workloads as W
+    dcfg = W.DECODE
+    dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, steps, 5, events_in_loop=False,
+                                            routings=routings)
+    nbytes, touched = decode_bytes(dcfg, dids)
+    return {"workload": "decode", "tokens": dcfg.T, "routings": routings, "us_per_step": dms * 1e3,
+            "touched_experts_mean": touched, "algorithmic_bytes_mean": nbytes,
+            "GBps": nbytes / (dms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "stage_us": {k: v * 1e3 for k, v in dstage.items()},
+            "finite": dfin}
+
+
+def time_skewed(nv, weights, steps, warmup):
+    """The skewed prefill batch (8192 tokens, Zipf-biased top-8 routing that
+    leaves experts empty, log-uniform per-expert alphas in [1e-4, 1e-2]) on the
+    same quantized weights with the config's alphas."""
+    import torch
+    import workloads as W
+    scfg = W.SKEWED
+    w13, w13sf, _, w2, w2sf, _ = weights
+    a13, a2 = W.alphas_loguniform(scfg)
+    sw = (w13, w13sf, torch.from_numpy(a13).cuda(), w2, w2sf, torch.from_numpy(a2).cuda())
+    ms, stage, s_valid, ids_np, fin = time_layer(nv, scfg, sw, steps, warmup)
+    import numpy as np
+    counts = np.bincount(ids_np[0].ravel(), minlength=scfg.E)
+    l1_flops = 2.0 * s_valid * scfg.H * 2 * scfg.I
+    return {"workload": "skewed prefill", "tokens": scfg.T, "slots": s_valid, "ms_per_step": ms,
+            "tokens_per_s": scfg.T / (ms * 1e-3),
+            "eff_tflops": 6.0 * s_valid * scfg.H * scfg.I / (ms * 1e-3) / 1e12,
+            "l1_f16_peak_frac": l1_flops / (stage["l1"] * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
+            "l2_f16_peak_frac": l1_flops / 2 / (stage["l2"] * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
+            "stage_ms": stage, "empty_experts": int((counts == 0).sum()),
+            "hottest_expert_slot_share": float(counts.max() / counts.sum()), "finite": fin}
+
+
+def time_dense_gemm(nv, launches=50):
+    """The single-expert dense GEMM (M 256, K 7168, N 6144): A quantized from
+    bf16 N(0,1)*3, B from N(0,0.02) by the library, prepacked; each timed
+    nvfp4_gemm call converts A to its f16 form and runs the GEMM. Timed with
+    events on torch's current stream (the binding launches there)."""
+    import torch
+    import workloads as W
+    cfg = W.DENSE
+    a, b = W.dense_gemm_inputs(cfg)
+    aq, asf, ags = nv.quantize(to_dev(a))
+    bq, bsf, balpha = nv.quantize_weights(to_dev(b)[None])
+    bq_t, bsf_t = nv.prepack_weights(bq, bsf)
+    out = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((nv._lib.nvfp4_gemm_workspace(cfg.M, cfg.N, cfg.K),), dtype=torch.uint8, device="cuda")
+    for _ in range(10):
+        nv.gemm(aq, asf, ags, bq_t[0], bsf_t[0], balpha, out=out, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        nv.gemm(aq, asf, ags, bq_t[0], bsf_t[0], balpha, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    flop = 2.0 * cfg.M * cfg.N * cfg.K
+    wbytes = cfg.K * cfg.N // 2 + cfg.K // 16 * cfg.N
+    return {"workload": "dense GEMM M 256 x K 7168 x N 6144", "us_per_call": us,
+            "tflops": flop / (us * 1e-6) / 1e12, "f16_peak_frac": flop / (us * 1e-6) / 1e12 / PEAK_F16_MFMA_TFLOPS,
+            "weight_GBps": wbytes / (us * 1e-6) / 1e9,
+            "note": "the 24.8 MB weight operand stays resident in the last-level cache across calls"}
 
 
 def _oracle_expert_weights(args):
@@ -189,12 +272,12 @@ def _oracle_expert_weights(args):
     return e, quantize_weight_bf16(w13), quantize_weight_bf16(w2)
 
 
-def cpu_baseline(cfg, experts=tuple(range(24))):
-    """The oracle's layer forward timed on a bounded sample of the prefill
-    workload: all T tokens' x, but only the slots routed to `experts` (the other
-    slots are skipped), with those experts' weights quantized by the oracle
-    beforehand (untimed, in spawned worker processes). Reported as
-    token-equivalents per second: sample slots / topk / seconds."""
+def cpu_baseline(cfg, experts=tuple(range(48))):
+    """The oracle's layer forward timed on the prefill workload: all T tokens'
+    x and the slots routed to `experts` (by default all 48, i.e. the whole
+    workload; the other slots would be skipped), with those experts' weights
+    quantized by the oracle beforehand (untimed, in spawned worker processes).
+    Reported as token-equivalents per second: sample slots / topk / seconds."""
     import multiprocessing as mp
     import numpy as np
     import workloads as W
@@ -229,10 +312,11 @@ def cpu_baseline(cfg, experts=tuple(range(24))):
     return {"value": slots / cfg.topk / dt, "unit": "tokens/s", "cores": cores,
             "blas_threads": blas_threads, "kind": "oracle", "seconds": dt,
             "sample": (f"prefill workload (T={cfg.T}, H={H}, I={I}, E={E}, top-{cfg.topk}): all "
-                       f"tokens' x quantized, only the {slots} slots routed to experts "
-                       f"{experts[0]}..{experts[-1]} run through L1/SiLU/requant/L2/combine; "
-                       f"value = slots/topk per second (token-equivalents); float64 BLAS matmuls "
-                       f"multithreaded, the rest single-threaded NumPy")}
+                       f"tokens' x quantized, the {slots} slots routed to experts "
+                       f"{experts[0]}..{experts[-1]} run through L1/SiLU/requant/L2/combine"
+                       f"{' (the whole workload)' if len(experts) == E else ''}; value = slots/topk "
+                       f"per second (token-equivalents); float64 BLAS matmuls multithreaded, the "
+                       f"rest single-threaded NumPy; the oracle's weight quantization is not timed")}
 
 
 def calibrate_copy():
@@ -269,17 +353,13 @@ def main():
     weights = make_weights(nv, cfg)
     setup_s = time.perf_counter() - t_setup
     if args.decode_only:
-        dcfg = W.DECODE
-        dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, args.decode_steps, 5,
-                                                events_in_loop=False)
-        nbytes, touched = decode_bytes(dcfg, dids)
-        print(json.dumps({"workload": "decode", "us_per_step": dms * 1e3, "GBps": nbytes / (dms * 1e-3) / 1e9,
-                          "stage_us": {k: v * 1e3 for k, v in dstage.items()}, "finite": dfin}), flush=True)
+        print(json.dumps(time_decode(nv, weights, args.decode_steps)), flush=True)
         return
     ms, stage_ms, s_valid, ids_np, finite = time_layer(nv, cfg, weights, args.steps, args.warmup)
     flops = 6.0 * s_valid * cfg.H * cfg.I
     l1_flops = 2.0 * s_valid * cfg.H * 2 * cfg.I
     l1_tflops = l1_flops / (stage_ms["l1"] * 1e-3) / 1e12
+    l2_tflops = (l1_flops / 2) / (stage_ms["l2"] * 1e-3) / 1e12
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -305,7 +385,10 @@ def main():
                    "intermediate": cfg.I, "experts": cfg.E, "topk": cfg.topk,
                    "slots": s_valid, "parallelism": "single GPU, one GPU's expert share"},
         "eff_tflops": flops / (ms * 1e-3) / 1e12,
+        "f16_peak_frac_layer": flops / (ms * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
         "stage_ms": stage_ms,
+        "l2_gemm": {"kernel": "L2 grouped GEMM (gemm_kernel<2>)", "achieved_tflops": l2_tflops,
+                    "f16_peak_frac": l2_tflops / PEAK_F16_MFMA_TFLOPS},
         "roofline": {"bound": "mfma", "kernel": "L1 grouped GEMM (gemm_kernel<1>)",
                      "achieved": l1_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": l1_tflops / PEAK_F16_MFMA_TFLOPS, "traffic": traffic,
@@ -322,17 +405,11 @@ def main():
         vms, vstage, _, _, vfin = time_layer(nv, cfg, weights, 10, 3, variant=variant)
         ext[variant] = {"ms_per_step": vms, "stage_ms": vstage, "finite": vfin}
     out["extensions"] = ext
+    # the other configurations of the workload recipe, each measured the same way
+    out["skewed"] = time_skewed(nv, weights, max(5, args.steps // 2), 2)
+    out["dense_gemm"] = time_dense_gemm(nv)
     if not args.no_decode:
-        dcfg = W.DECODE
-        dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, args.decode_steps, 5,
-                                                events_in_loop=False)
-        nbytes, touched = decode_bytes(dcfg, dids)
-        out["decode"] = {"workload": "decode", "tokens": dcfg.T, "us_per_step": dms * 1e3,
-                         "touched_experts": touched, "algorithmic_bytes": nbytes,
-                         "GBps": nbytes / (dms * 1e-3) / 1e9,
-                         "hbm_frac": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                         "stage_us": {k: v * 1e3 for k, v in dstage.items()},
-                         "finite": dfin}
+        out["decode"] = time_decode(nv, weights, args.decode_steps)
     del weights
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -45,6 +45,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
 struct MoeLayout {
     size_t off[NVFP4_MOE_WS_NUM];
     size_t amax;        // 2 x uint32: x amax, act amax
+    size_t partials;    // kRouteMaxPartials x uint32: partial maxima of x
+    size_t wg_counts;   // kRouteMaxChunks x E int32: routing chunk counts
     size_t tiles;
     size_t num_tiles;
     size_t total;
@@ -85,6 +87,10 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int64_t topk) {
     }
     L.amax = cur;
     cur = align_up(cur + 8);
+    L.partials = cur;
+    cur = align_up(cur + 4 * kRouteMaxPartials);
+    L.wg_counts = cur;
+    cur = align_up(cur + 4 * (size_t)kRouteMaxChunks * (size_t)E);
     L.max_tiles = moe_max_tiles(S, E, kSkinnyBM);     // the larger of the two tile lists
     L.tiles = cur;
     cur = align_up(cur + sizeof(Tile) * (size_t)(L.max_tiles > 0 ? L.max_tiles : 1));
@@ -398,19 +404,31 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
 
     // 1 + 2. routing tables + tile list, and the quantization of x in further
     // work-groups of the same launch, concurrently with the routing (stage 2
-    // is then empty). A larger x (and no static scale) first gets its amax
-    // from the amax kernel; a small one is reduced by the quantization
-    // work-groups themselves. The routing launch zeroes the act amax slot.
+    // is then empty). A larger x (and no static scale) first gets its partial
+    // maxima from the pre-pass, which also counts the slots of every routing
+    // chunk of a larger batch; a small x is reduced by the quantization
+    // work-groups themselves, a small batch counted by its one routing
+    // work-group. The routing launch zeroes the act amax slot.
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_ROUTE));
     const bool small_x = T * H <= kSmallQuantMax;
     const bool amax_pass = !small_x && !x_gs;
-    if (amax_pass) {
-        NVFP4_TRY(launch_zero_u32(amax, 1, stream));
-        NVFP4_TRY(launch_amax_bf16(x, T * H, amax, stream));
-    }
-    const SmallQuant sq = {x,   x_gs,        amax_pass ? amax : nullptr, T, H, xq, pitch_q(H), xsf,
-                           pitch_sf(H), gs1, skinny ? nullptr : xh};
-    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, counts, offsets, sorted_slot,
+    uint32_t* partials = reinterpret_cast<uint32_t*>(ws + L.partials);
+    int32_t* wg_counts = reinterpret_cast<int32_t*>(ws + L.wg_counts);
+    NVFP4_TRY(launch_route_prepass(amax_pass ? x : nullptr, T * H, partials, topk_ids, S, (int)E, wg_counts,
+                                   stream));
+    const SmallQuant sq = {x,
+                           x_gs,
+                           amax_pass ? partials : nullptr,
+                           amax_pass ? route_amax_partials(T * H) : 0,
+                           T,
+                           H,
+                           xq,
+                           pitch_q(H),
+                           xsf,
+                           pitch_sf(H),
+                           gs1,
+                           skinny ? nullptr : xh};
+    NVFP4_TRY(launch_route(topk_ids, S, (int)topk, (int)E, BM, wg_counts, counts, offsets, sorted_slot,
                            slot_row, tiles, num_tiles, amax + 1, 1, &sq, stream));
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_QUANT_X));
     // 3. L1 grouped GEMM with fused SiLU(gate) * up

@@ -119,14 +119,15 @@ hipError_t launch_quant_cols(const uint16_t* w, int64_t E, int64_t K, int64_t N,
                              hipStream_t s);
 
 // Quantization of the activation done inside the routing launch by extra
-// work-groups, concurrently with the routing work-group: each takes the global
-// scale from gs_in (static), else from the amax in *amax_in (computed by an
-// earlier launch), else reduces the whole amax itself (small inputs), then
+// work-groups, concurrently with the routing work-groups: each takes the
+// global scale from gs_in (static), else from the maximum of the pre-pass's
+// partial maxima, else reduces the whole amax itself (small inputs), then
 // quantizes its share of the 16-element blocks.
 struct SmallQuant {
     const uint16_t* x;
     const float* gs_in;      // static global scale, or null
-    const uint32_t* amax_in; // amax as float bits, or null
+    const uint32_t* amax_partials;  // partial maxima (bf16 magnitude bits) of x, or null
+    int n_partials;
     int64_t M, K;
     uint8_t* q;
     int64_t ldq;
@@ -137,11 +138,30 @@ struct SmallQuant {
 };
 constexpr int64_t kSmallQuantMax = 1 << 17;   // elements: larger inputs take the two-kernel path
 
-// Routing tables and the tile list (one work-group), plus the quantization of
-// *xq when xq is not null. Also zeroes `zero_slots` (n_zero words) before
-// anything else in the layer runs.
-hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
+// Routing in chunks: up to kRouteChunk slots take one routing work-group
+// (which counts them itself); more take one work-group per chunk of
+// route_chunk(S) slots (at most kRouteMaxChunks chunks), whose counts the
+// pre-pass provides.
+constexpr int64_t kRouteChunk = 4096;
+constexpr int64_t kRouteMaxChunks = 64;
+constexpr int kRouteMaxPartials = 256;
+int64_t route_chunk(int64_t S);
+// number of partial maxima the pre-pass writes for n activation values
+int route_amax_partials(int64_t n);
+
+// Pre-pass of the routing launch: when x is not null, the partial maxima of
+// its n bf16 values (route_amax_partials(n) words into `partial`); when S >
+// kRouteChunk, the per-expert counts of every chunk of slots into wg_counts
+// (chunks x E int32).
+hipError_t launch_route_prepass(const uint16_t* x, int64_t n, uint32_t* partial, const int32_t* ids,
+                                int64_t S, int E, int32_t* wg_counts, hipStream_t s);
+
+// Routing tables and the tile list, plus the quantization of *xq when xq is
+// not null (further work-groups of the same launch). Also zeroes `zero_slots`
+// (n_zero words) before anything else in the layer runs. wg_counts: the
+// pre-pass's chunk counts (used when S > kRouteChunk).
+hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, const int32_t* wg_counts,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
                         int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
                         hipStream_t s);
 

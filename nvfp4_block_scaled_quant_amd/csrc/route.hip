@@ -25,33 +25,104 @@ namespace {
 
 constexpr int kWaves = kRouteThreads / 64;
 constexpr int kIdBatches = 16;     // batches of 64 ids a lane holds at once
+constexpr int kPreThreads = 256;   // threads of the pre-pass work-groups
 
-// Dynamic LDS: cnt[E], off[E+1], run[E], wcnt[kWaves][E]
+// The pre-pass of a large layer input: work-groups [0, n_amax) reduce the
+// amax of x (n bf16 values, n % 8 == 0) to one partial maximum each (bf16
+// magnitude bits, partial[b]); work-groups from n_amax on count the expert ids
+// of one chunk of C slots each (wg_counts[g][e], ids outside [0, E) not
+// counted). Partials instead of one atomic slot: the readers take the maximum
+// of at most 256 words, and nothing needs zeroing first.
+__global__ __launch_bounds__(kPreThreads) void route_prepass_kernel(
+    const uint16_t* __restrict__ x, int64_t n, int n_amax, uint32_t* __restrict__ partial,
+    const int32_t* __restrict__ ids, int64_t S, int E, int64_t C, int32_t* __restrict__ wg_counts) {
+    __shared__ uint32_t red[kPreThreads / 64];
+    extern __shared__ int32_t hist[];
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < n_amax) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(x);
+        const int64_t nvec = n / 8, stride = (int64_t)n_amax * kPreThreads;
+        uint32_t m = 0;
+        for (int64_t i0 = (int64_t)blockIdx.x * kPreThreads + tid; i0 < nvec; i0 += 4 * stride) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t i = i0 + u * stride;
+                v[u] = i < nvec ? p[i] : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) m = max(m, max(v[u][c] & 0x7FFFu, (v[u][c] >> 16) & 0x7FFFu));
+        }
+        m = wave_max_u32(m);
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        if (tid == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+        return;
+    }
+    const int64_t g = blockIdx.x - n_amax;
+    for (int e = tid; e < E; e += kPreThreads) hist[e] = 0;
+    __syncthreads();
+    const int64_t lo = g * C, hi = min(S, lo + C);
+    // all of a thread's ids are loaded before any is counted
+    constexpr int kPer = 16;
+    int idr[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int64_t sl = lo + (int64_t)u * kPreThreads + tid;
+        idr[u] = sl < hi ? ids[sl] : -1;
+    }
+    for (int64_t b = lo + kPer * kPreThreads; ; b += kPer * kPreThreads) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            if (idr[u] >= 0 && idr[u] < E) atomicAdd(&hist[idr[u]], 1);
+        if (b >= hi) break;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int64_t sl = b + (int64_t)u * kPreThreads + tid;
+            idr[u] = sl < hi ? ids[sl] : -1;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPreThreads) wg_counts[g * E + e] = hist[e];
+}
+
+// Dynamic LDS: cnt[E], off[E+1], base[E], wcnt[kWaves][E]
+//
+// Routing work-groups 0 .. G-1, each over the slots [g C, (g+1) C): with
+// wg_counts (the pre-pass's chunk counts) every one of them derives the
+// global per-expert counts and its own chunk's base per expert; without
+// (G = 1, C = S) the single work-group counts everything itself. Work-group 0
+// writes counts, offsets and the tile list. Work-groups G.. quantize x.
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    const int32_t* __restrict__ ids, int64_t S, int E, int BM, int nbits,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
-    int32_t* __restrict__ slot_row, Tile* __restrict__ tiles, int32_t* __restrict__ num_tiles,
-    uint32_t* __restrict__ zero_slots, int n_zero, SmallQuant xq) {
-    if (blockIdx.x > 0) {
+    const int32_t* __restrict__ ids, int64_t S, int E, int BM, int nbits, int64_t C, int G,
+    const int32_t* __restrict__ wg_counts, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ slot_row, Tile* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles, uint32_t* __restrict__ zero_slots, int n_zero, SmallQuant xq) {
+    if ((int)blockIdx.x >= G) {
         // quantization work-groups: the global scale is static, or comes from
-        // an amax computed before this launch, or (a small activation: a few
+        // the pre-pass's partial maxima, or (a small activation: a few
         // hundred KB at most, from L2) every work-group reduces the amax of all
         // of x itself; then each quantizes its share of the 16-element blocks
         __shared__ uint32_t wmax[kWaves];
         const int tid = threadIdx.x;
+        const int qb = blockIdx.x - G;
         QuantScales qs;
         if (xq.gs_in) {
             qs = scales_from_gs(*xq.gs_in);
-        } else if (xq.amax_in) {
-            qs = make_scales(__uint_as_float(*xq.amax_in));
         } else {
-            const int64_t n = xq.M * xq.K;
-            const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
             uint32_t m = 0;
-            for (int64_t i = tid; i < n / 8; i += kRouteThreads) {
-                const u32x4 w = v[i];
+            if (xq.amax_partials) {
+                for (int i = tid; i < xq.n_partials; i += kRouteThreads) m = max(m, xq.amax_partials[i]);
+            } else {
+                const int64_t n = xq.M * xq.K;
+                const u32x4* v = reinterpret_cast<const u32x4*>(xq.x);
+                for (int64_t i = tid; i < n / 8; i += kRouteThreads) {
+                    const u32x4 w = v[i];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7FFFu, (w[c] >> 16) & 0x7FFFu));
+                    for (int c = 0; c < 4; ++c) m = max(m, max(w[c] & 0x7FFFu, (w[c] >> 16) & 0x7FFFu));
+                }
             }
             m = wave_max_u32(m);
             if ((tid & 63) == 0) wmax[tid >> 6] = m;
@@ -60,29 +131,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             for (int w = 1; w < kWaves; ++w) m = max(m, wmax[w]);
             qs = make_scales(__uint_as_float(m << 16));
         }
-        if (blockIdx.x == 1 && tid == 0) *xq.gs = qs.gs;
+        if (qb == 0 && tid == 0) *xq.gs = qs.gs;
         const int64_t groups = xq.K / 16;
-        for (int64_t b = (int64_t)(blockIdx.x - 1) * kRouteThreads + tid; b < xq.M * groups;
-             b += (int64_t)(gridDim.x - 1) * kRouteThreads)
+        for (int64_t b = (int64_t)qb * kRouteThreads + tid; b < xq.M * groups;
+             b += (int64_t)(gridDim.x - G) * kRouteThreads)
             quantize_row_block(xq.x, b, groups, qs, xq.q, xq.ldq, xq.sf, xq.ldsf,
                                reinterpret_cast<uint8_t*>(xq.h));
         return;
     }
     extern __shared__ int32_t lds[];
-    int32_t* cnt = lds;
-    int32_t* off = cnt + E;
-    int32_t* wcnt = off + E + 1;                     // [kWaves][E]: counts, then running positions
+    int32_t* cnt = lds;                              // global count per expert
+    int32_t* off = cnt + E;                          // global first sorted row per expert
+    int32_t* gbase = off + E + 1;                    // this chunk's first row per expert, past off
+    int32_t* wcnt = gbase + E;                       // [kWaves][E]: counts, then running positions
     __shared__ int32_t tile_base[kMaxExperts + 1];   // first full tile of each expert
     __shared__ int32_t part_base[kMaxExperts + 1];   // its partial tile (after all full ones)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    // wave w owns the contiguous slot range [s_lo, s_hi): the sorted order is
-    // stable because the waves' ranges are in slot order and each wave scatters
-    // its own range in order
-    const int64_t per = (S + kWaves - 1) / kWaves;
-    const int64_t s_lo = min(S, (int64_t)wave * per), s_hi = min(S, s_lo + per);
-    for (int i = tid; i < n_zero; i += kRouteThreads) zero_slots[i] = 0u;
+    const int g = blockIdx.x;
+    const int64_t c_lo = (int64_t)g * C, c_hi = min(S, c_lo + C);
+    // wave w owns the contiguous slot range [s_lo, s_hi) of this chunk: the
+    // sorted order is stable because the chunks and the waves' ranges are in
+    // slot order and each wave scatters its own range in order
+    const int64_t per = (c_hi - c_lo + kWaves - 1) / kWaves;
+    const int64_t s_lo = min(c_hi, c_lo + (int64_t)wave * per), s_hi = min(c_hi, s_lo + per);
+    if (g == 0)
+        for (int i = tid; i < n_zero; i += kRouteThreads) zero_slots[i] = 0u;
     for (int i = tid; i < kWaves * E; i += kRouteThreads) wcnt[i] = 0;
     __syncthreads();
 
@@ -107,7 +182,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         }
     }
     __syncthreads();
-    // totals, and each wave's exclusive base within an expert
+    // chunk counts and each wave's exclusive base within an expert; global
+    // counts and this chunk's base among the chunks
     for (int e = tid; e < E; e += kRouteThreads) {
         int acc = 0;
         for (int w = 0; w < kWaves; ++w) {
@@ -115,7 +191,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             wcnt[w * E + e] = acc;
             acc += c;
         }
-        cnt[e] = acc;
+        if (wg_counts) {
+            int before = 0, total = 0;
+            for (int h = 0; h < G; ++h) {
+                const int c = wg_counts[(int64_t)h * E + e];
+                before += (h < g) ? c : 0;
+                total += c;
+            }
+            cnt[e] = total;
+            gbase[e] = before;
+        } else {
+            cnt[e] = acc;
+            gbase[e] = 0;
+        }
     }
     __syncthreads();
 
@@ -149,29 +237,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
             off[E] = acc;
             tile_base[E] = facc;         // number of full tiles
             part_base[E] = pacc;
-            *num_tiles = facc + pacc;
+            if (g == 0) *num_tiles = facc + pacc;
         }
     }
     __syncthreads();
-    for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
-    for (int e = tid; e < E; e += kRouteThreads) {
-        counts[e] = cnt[e];
-        const int nf = cnt[e] / BM;
-        for (int i = 0; i <= nf; ++i) {
-            Tile t;
-            t.expert = e;
-            t.row_start = off[e] + i * BM;
-            t.row_count = min(BM, cnt[e] - i * BM);
-            t.pad = 0;
-            if (i < nf) tiles[tile_base[e] + i] = t;
-            else if (t.row_count > 0) tiles[tile_base[E] + part_base[e]] = t;
+    if (g == 0) {
+        for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
+        for (int e = tid; e < E; e += kRouteThreads) {
+            counts[e] = cnt[e];
+            const int nf = cnt[e] / BM;
+            for (int i = 0; i <= nf; ++i) {
+                Tile t;
+                t.expert = e;
+                t.row_start = off[e] + i * BM;
+                t.row_count = min(BM, cnt[e] - i * BM);
+                t.pad = 0;
+                if (i < nf) tiles[tile_base[e] + i] = t;
+                else if (t.row_count > 0) tiles[tile_base[E] + part_base[e]] = t;
+            }
         }
     }
 
     // stable scatter, wave by wave with no further barrier: 64 slots at a time,
-    // a slot's position is its expert's start + this wave's base + the slots of
-    // the same expert before it (earlier batches: the running count in LDS;
-    // this batch: lanes below it with the same id, matched bit by bit)
+    // a slot's position is its expert's start + this chunk's base + this
+    // wave's base + the slots of the same expert before it (earlier batches:
+    // the running count in LDS; this batch: lanes below it with the same id,
+    // matched bit by bit)
     int32_t* run = wcnt + wave * E;
     for (int64_t c00 = s_lo; c00 < s_hi; c00 += 64 * kIdBatches) {
       load_ids(c00);
@@ -192,7 +283,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         const int rank = __popcll(match & below);
         const int total = __popcll(match);
         if (valid) {
-            const int pos = off[e] + run[e] + rank;
+            const int pos = off[e] + gbase[e] + run[e] + rank;
             sorted_slot[pos] = (int32_t)s;
             slot_row[s] = pos;
         } else if (s < s_hi) {
@@ -338,20 +429,46 @@ __global__ __launch_bounds__(64 * kTopkWaves) void route_topk_kernel(
 
 }  // namespace
 
-hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, int32_t* counts,
-                        int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
+int64_t route_chunk(int64_t S) {
+    const int64_t c = (S + kRouteMaxChunks - 1) / kRouteMaxChunks;
+    return c <= kRouteChunk ? kRouteChunk : (c + 1023) / 1024 * 1024;
+}
+
+int route_amax_partials(int64_t n) {
+    const int64_t b = (n / 8 + kPreThreads - 1) / kPreThreads;
+    return (int)(b < kRouteMaxPartials ? b : kRouteMaxPartials);
+}
+
+hipError_t launch_route_prepass(const uint16_t* x, int64_t n, uint32_t* partial, const int32_t* ids,
+                                int64_t S, int E, int32_t* wg_counts, hipStream_t s) {
+    const int n_amax = x ? route_amax_partials(n) : 0;
+    const int64_t C = route_chunk(S);
+    const int64_t G = (S > kRouteChunk) ? (S + C - 1) / C : 0;
+    if (n_amax + G == 0) return hipSuccess;
+    route_prepass_kernel<<<(unsigned)(n_amax + G), kPreThreads, sizeof(int32_t) * E, s>>>(
+        x, n, n_amax, partial, ids, S, E, C, wg_counts);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_route(const int32_t* ids, int64_t S, int topk, int E, int BM, const int32_t* wg_counts,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* slot_row, Tile* tiles,
                         int32_t* num_tiles, uint32_t* zero_slots, int n_zero, const SmallQuant* xq,
                         hipStream_t s) {
     (void)topk;
     int nbits = 1;
     while ((1 << nbits) < E) ++nbits;
-    const size_t lds = sizeof(int32_t) * ((size_t)E * (2 + kWaves) + 1);
+    const size_t lds = sizeof(int32_t) * ((size_t)E * (3 + kWaves) + 1);
     const SmallQuant none = {};
-    // work-groups 1.. quantize the activation, one 16-element block per thread
+    // one routing work-group per chunk when the pre-pass counted the chunks,
+    // else one for everything; then the quantization of the activation, one
+    // 16-element block per thread
+    const int64_t C = (S > kRouteChunk) ? route_chunk(S) : (S > 0 ? S : 1);
+    const int G = (S > kRouteChunk) ? (int)((S + C - 1) / C) : 1;
     const int64_t qgroups = xq ? (xq->M * (xq->K / 16) + kRouteThreads - 1) / kRouteThreads : 0;
-    route_kernel<<<(unsigned)(1 + qgroups), kRouteThreads, lds, s>>>(ids, S, E, BM, nbits, counts, offsets, sorted_slot,
-                                                        slot_row, tiles, num_tiles, zero_slots, n_zero,
-                                                        xq ? *xq : none);
+    route_kernel<<<(unsigned)(G + qgroups), kRouteThreads, lds, s>>>(
+        ids, S, E, BM, nbits, C, G, (S > kRouteChunk) ? wg_counts : nullptr, counts, offsets, sorted_slot,
+        slot_row, tiles, num_tiles, zero_slots, n_zero, xq ? *xq : none);
     return hipGetLastError();
 }
 

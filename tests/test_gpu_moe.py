@@ -149,6 +149,24 @@ def test_small_batch_shapes(nv, T, H, I, E, k):
     compare_layer(nv, make_layer(cfg), f"small-batch T{T} H{H} I{I} E{E} k{k}")
 
 
+# batches above one routing chunk (4096 slots) are routed by one work-group
+# per chunk after a counting pre-pass: one slot past a chunk, three chunks
+# with skipped ids on the chunk boundaries, and enough slots (264,000) for the
+# chunk to grow past 4096 (52 chunks of 5120)
+@pytest.mark.parametrize("T,H,I,E,k,skip", [(4097, 128, 16, 5, 1, False), (1100, 256, 128, 16, 8, True),
+                                            (33000, 128, 16, 8, 8, False)])
+def test_routing_chunks(nv, T, H, I, E, k, skip):
+    cfg = W.small_layer(f"chunks{T}", T=T, H=H, I=I, E=E, topk=k, seed=T + E)
+    L = make_layer(cfg)
+    if skip:
+        ids = L["ids"].copy().ravel()
+        for b in (4095, 4096, 8191, 8192, 8799):
+            ids[b] = -1 if b % 2 else E + 3
+        L["ids"] = ids.reshape(T, k)
+    g, _, _ = compare_layer(nv, L, f"routing chunks T{T} k{k}")
+    assert g["counts"].sum() == ((L["ids"] >= 0) & (L["ids"] < E)).sum()
+
+
 def test_skipped_ids_and_empty_experts(nv):
     cfg = W.small_layer("skip", T=90, H=256, I=128, E=6, topk=3, seed=9)
     L = make_layer(cfg)
