@@ -42,7 +42,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
-                    help="skip the prefill timing (profiling runs of the decode batch)")
+                    help="only the decode batch (profiling runs)")
+    ap.add_argument("--only", choices=("prefill", "skewed", "dense", "decode"), default=None,
+                    help="run one measurement and print its JSON (profiling runs)")
+    ap.add_argument("--no-graph", action="store_true", help="decode: skip the HIP-graph timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (for PMC byte-counter scaling)")
     return ap.parse_args()
@@ -192,7 +195,7 @@ def decode_bytes(cfg, ids_np):
     return touched * per_expert + cfg.T * H * 2 * 2 + act, touched
 
 
-def time_decode(nv, weights, steps, routings=8):
+def time_decode(nv, weights, steps, routings=8, graph=True):
     """The decode batch (8 tokens, top-8 of 48) cycling through `routings`
     seeded routings, so that consecutive steps touch different expert sets;
     bytes are the routings' mean algorithmic weight bytes."""
@@ -201,12 +204,47 @@ def time_decode(nv, weights, steps, routings=8):
     dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, steps, 5, events_in_loop=False,
                                             routings=routings)
     nbytes, touched = decode_bytes(dcfg, dids)
+    g_us = time_decode_graph(nv, weights, routings=routings) if graph else None
     return {"workload": "decode", "tokens": dcfg.T, "routings": routings, "us_per_step": dms * 1e3,
+            "graph_us_per_step": g_us, "graph_GBps": nbytes / (g_us * 1e-6) / 1e9 if g_us else None,
             "touched_experts_mean": touched, "algorithmic_bytes_mean": nbytes,
             "GBps": nbytes / (dms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "stage_us": {k: v * 1e3 for k, v in dstage.items()},
             "finite": dfin}
+
+
+def time_decode_graph(nv, weights, replays=400, routings=8):
+    """The decode batch captured in HIP graphs: one graph per seeded routing,
+    each one nvfp4_moe_forward_noalloc call (the allocation-free entry point,
+    workspace in the library's static scratch), replayed round-robin; timed
+    with events on torch's current stream. Returns microseconds per step."""
+    import dataclasses
+    import torch
+    import workloads as W
+    dcfg = W.DECODE
+    x = to_dev(W.activations(dcfg))
+    y = torch.empty((dcfg.T, dcfg.H), dtype=torch.bfloat16, device="cuda")
+    routes = [tuple(to_dev(a) for a in W.routing(dataclasses.replace(dcfg, seed_x=dcfg.seed_x + r)))
+              for r in range(routings)]
+    nv.moe_forward_noalloc(x, *routes[0], *weights, y=y)      # set-up outside the capture
+    torch.cuda.synchronize()
+    graphs = []
+    for ids, wts in routes:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            nv.moe_forward_noalloc(x, ids, wts, *weights, y=y)
+        graphs.append(g)
+    for i in range(2 * routings):
+        graphs[i % routings].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(replays):
+        graphs[i % routings].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / replays
 
 
 def time_skewed(nv, weights, steps, warmup):
@@ -320,16 +358,19 @@ def cpu_baseline(cfg, experts=tuple(range(48))):
 
 
 def calibrate_copy():
+    """Device copies of 1 GiB and of 256 MiB (three each), whose PMC byte
+    counters give the scaling of FETCH_SIZE and WRITE_SIZE to bytes."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
-    b = torch.empty_like(a)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+    for n in (1 << 30, 1 << 28):
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+        del a, b
 
 
 def main():
@@ -352,8 +393,18 @@ def main():
     t_setup = time.perf_counter()
     weights = make_weights(nv, cfg)
     setup_s = time.perf_counter() - t_setup
-    if args.decode_only:
-        print(json.dumps(time_decode(nv, weights, args.decode_steps)), flush=True)
+    if args.decode_only or args.only == "decode":
+        print(json.dumps(time_decode(nv, weights, args.decode_steps, graph=not args.no_graph)), flush=True)
+        return
+    if args.only == "skewed":
+        print(json.dumps(time_skewed(nv, weights, args.steps, args.warmup)), flush=True)
+        return
+    if args.only == "dense":
+        print(json.dumps(time_dense_gemm(nv)), flush=True)
+        return
+    if args.only == "prefill":
+        ms, stage_ms, _, _, _ = time_layer(nv, cfg, weights, args.steps, args.warmup)
+        print(json.dumps({"workload": "prefill", "ms_per_step": ms, "stage_ms": stage_ms}), flush=True)
         return
     ms, stage_ms, s_valid, ids_np, finite = time_layer(nv, cfg, weights, args.steps, args.warmup)
     flops = 6.0 * s_valid * cfg.H * cfg.I
