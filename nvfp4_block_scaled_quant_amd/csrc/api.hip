@@ -279,10 +279,13 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
 }
 
 // ---------------------------------------------------------------------------
+// A's f16 form, then (when K is cut into chunks) the chunks' partial sums
+size_t gemm_ws_partial_offset(int64_t M, int64_t K) { return align_up((size_t)((M > 0 ? M : 1) * pitch_h(K))); }
+
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K) {
-    (void)N;
-    if (M < 0 || K <= 0 || K % 16) return 0;
-    return align_up((size_t)((M > 0 ? M : 1) * pitch_h(K)));
+    if (M < 0 || N <= 0 || K <= 0 || K % 16) return 0;
+    const int ks = dense_ksplit(M, N, K);
+    return gemm_ws_partial_offset(M, K) + (ks > 1 ? align_up((size_t)ks * (size_t)M * (size_t)N * 4) : 0);
 }
 
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const uint8_t* bq,
@@ -317,7 +320,12 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs, const u
     p.a_gs = a_gs;
     p.b_alpha = b_alpha;
     p.out_bf16 = out;
-    return hip_status(launch_gemm(p, stream));
+    // too few tiles to fill the GPU: K in chunks, partial sums, then one reduction
+    p.ksplit = dense_ksplit(M, N, K);
+    p.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + gemm_ws_partial_offset(M, K));
+    NVFP4_TRY(launch_gemm(p, stream));
+    if (p.ksplit > 1) NVFP4_TRY(launch_splitk_reduce(p.partial, p.ksplit, M, N, a_gs, b_alpha, out, stream));
+    return NVFP4_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -435,6 +443,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L1));
     GemmParams p1 = {};
     p1.mode = kGemmL1;
+    p1.ksplit = 1;
     p1.aq = xq;
     p1.asf = xsf;
     p1.ah = xh;
@@ -464,6 +473,7 @@ int nvfp4_moe_forward_ex(const uint16_t* x, const int32_t* topk_ids, const float
     NVFP4_TRY(mark(NVFP4_MOE_STAGE_L2));
     GemmParams p2 = {};
     p2.mode = kGemmL2;
+    p2.ksplit = 1;
     p2.aq = aq;
     p2.asf = asf;
     p2.ah = ah;

@@ -110,10 +110,23 @@ void gemm_kernel(GemmParams p) {
     const int64_t ldq = pitch_q(K), lda = pitch_h(K);           // packed B row, f16 A row
     const int64_t ldwsf = pitch_wsf(K);                         // packed weight scales
     const int ntn = (MODE == kGemmL1) ? (int)((p.I + 127) / 128) : (int)((N + BN - 1) / BN);
-    const int xcd = blockIdx.x & 7;
-    const int slot = blockIdx.x >> 3;
-    const int tile_idx = 8 * (slot / ntn) + xcd;
-    const int nt = slot % ntn;
+    // Grouped GEMMs: XCD order (above). Dense: plain order, tile fastest, then
+    // N-tile, then K chunk (with ksplit > 1, chunk c sums the c-th range of K
+    // steps into its own partial sums): the dense shapes have few tiles, which
+    // the XCD order would put on one XCD.
+    int tile_idx, nt, chunk = 0;
+    if (MODE == kGemmDense) {
+        const int mt = (int)((p.M + BM - 1) / BM);
+        tile_idx = blockIdx.x % mt;
+        const int rest = blockIdx.x / mt;
+        nt = rest % ntn;
+        chunk = rest / ntn;
+    } else {
+        const int xcd = blockIdx.x & 7;
+        const int slot = blockIdx.x >> 3;
+        tile_idx = 8 * (slot / ntn) + xcd;
+        nt = slot % ntn;
+    }
 
     int expert, row_start, row_count;
     if (MODE == kGemmDense) {
@@ -197,7 +210,13 @@ void gemm_kernel(GemmParams p) {
             bsf_off[t] = (uint32_t)((n >> 4) * 16 * ldwsf + (n & 15) * 32 + (lane & 1) * 8);
         }
 
-        const int nk = (int)(ldq / 32);             // 64-element steps
+        // 64-element steps: all of K, or this work-group's chunk [kb, kb + nk)
+        // (dense_ksplit makes every chunk non-empty)
+        const int nk_all = (int)(ldq / 32);
+        const bool split = MODE == kGemmDense && p.ksplit > 1;
+        const int kper = split ? (nk_all + p.ksplit - 1) / p.ksplit : nk_all;
+        const int kb = split ? chunk * kper : 0;
+        const int nk = split ? min(nk_all, kb + kper) - kb : nk_all;
         // ---- main loop ---------------------------------------------------------
         const int wm = wave >> 1, wn = wave & 1;
         const int l32 = lane & 31, h = lane >> 5;
@@ -252,7 +271,8 @@ void gemm_kernel(GemmParams p) {
         // load j (0..3) of part t of the DMA of stage ks (none when that part
         // has fewer loads): part t < 2 holds A loads t MI .. t MI + MI - 1,
         // part 2 the two B loads and the two scale loads
-        auto issue_one = [&](int ks, int st, int t, int j) {
+        auto issue_one = [&](int ksr, int st, int t, int j) {
+            const int ks = kb + ksr;                   // absolute step
             uint8_t* base = smem_raw + st * STAGE_BYTES;
             if (t < 2) {
                 if (j < MI)
@@ -382,6 +402,50 @@ void gemm_kernel(GemmParams p) {
         step(ks, P2{}, ks % NSTAGE);
         __syncthreads();
 
+        // float32 rows of the tile (L2's output, or a dense K chunk's partial
+        // sums): scale * acc to out (rows of N)
+        auto store_f32 = [&](float* __restrict__ out, float scale) {
+            // A lane holds four consecutive rows of one column per group of
+            // four accumulator registers. A 4 x 4 transpose inside each quad of
+            // lanes (two butterfly stages of quad-permute DPP moves) gives lane
+            // 4c + m row m of that group at columns 4c .. 4c + 3, so every
+            // store writes 16 contiguous bytes: 64 stores per lane instead of
+            // 256 (the per-wave limit of 63 outstanding memory operations
+            // otherwise stalls the epilogue on store latency several times).
+            const int m = l32 & 3;
+            const bool odd = (m & 1) != 0, upper = (m & 2) != 0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int local = wm * (32 * MI) + 32 * i + 8 * g + 4 * h + m;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float v0 = scale * acc[i][j][4 * g], v1 = scale * acc[i][j][4 * g + 1];
+                        float v2 = scale * acc[i][j][4 * g + 2], v3 = scale * acc[i][j][4 * g + 3];
+                        // stage 1 (lanes m, m ^ 1): even lanes take the partner's
+                        // v0 / v2 into v1 / v3, odd lanes its v1 / v3 into v0 / v2
+                        const float s1a = odd ? v0 : v1, s1b = odd ? v2 : v3;
+                        const float r1a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s1a), 0xB1, 0xF, 0xF, false));   // quad_perm(1,0,3,2)
+                        const float r1b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s1b), 0xB1, 0xF, 0xF, false));
+                        if (odd) { v0 = r1a; v2 = r1b; } else { v1 = r1a; v3 = r1b; }
+                        // stage 2 (lanes m, m ^ 2): pairs (v0, v1) <-> (v2, v3)
+                        const float s2a = upper ? v0 : v2, s2b = upper ? v1 : v3;
+                        const float r2a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s2a), 0x4E, 0xF, 0xF, false));   // quad_perm(2,3,0,1)
+                        const float r2b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, s2b), 0x4E, 0xF, 0xF, false));
+                        if (upper) { v0 = r2a; v1 = r2b; } else { v2 = r2a; v3 = r2b; }
+                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + 4 * (l32 >> 2);
+                        if (local < row_count && col < N)   // N % 16 == 0: four columns are in or out together
+                            *reinterpret_cast<float4_t*>(out + (row_start + local) * N + col) =
+                                (float4_t){v0, v1, v2, v3};
+                    }
+                }
+            }
+        };
         // ---- epilogue ------------------------------------------------------------
         // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
         // L1 with per-half weight scales: gate columns take alpha, up alpha_up
@@ -507,46 +571,9 @@ void gemm_kernel(GemmParams p) {
                 atomicMax(p.amax_slot, m << 16);
             }
         } else if (MODE == kGemmL2) {
-            // A lane holds four consecutive rows of one column per group of
-            // four accumulator registers. A 4 x 4 transpose inside each quad of
-            // lanes (two butterfly stages of quad-permute DPP moves) gives lane
-            // 4c + m row m of that group at columns 4c .. 4c + 3, so every
-            // store writes 16 contiguous bytes: 64 stores per lane instead of
-            // 256 (the per-wave limit of 63 outstanding memory operations
-            // otherwise stalls the epilogue on store latency several times).
-            const int m = l32 & 3;
-            const bool odd = (m & 1) != 0, upper = (m & 2) != 0;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int local = wm * (32 * MI) + 32 * i + 8 * g + 4 * h + m;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float v0 = alpha * acc[i][j][4 * g], v1 = alpha * acc[i][j][4 * g + 1];
-                        float v2 = alpha * acc[i][j][4 * g + 2], v3 = alpha * acc[i][j][4 * g + 3];
-                        // stage 1 (lanes m, m ^ 1): even lanes take the partner's
-                        // v0 / v2 into v1 / v3, odd lanes its v1 / v3 into v0 / v2
-                        const float s1a = odd ? v0 : v1, s1b = odd ? v2 : v3;
-                        const float r1a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                            __builtin_bit_cast(int, s1a), 0xB1, 0xF, 0xF, false));   // quad_perm(1,0,3,2)
-                        const float r1b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                            __builtin_bit_cast(int, s1b), 0xB1, 0xF, 0xF, false));
-                        if (odd) { v0 = r1a; v2 = r1b; } else { v1 = r1a; v3 = r1b; }
-                        // stage 2 (lanes m, m ^ 2): pairs (v0, v1) <-> (v2, v3)
-                        const float s2a = upper ? v0 : v2, s2b = upper ? v1 : v3;
-                        const float r2a = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                            __builtin_bit_cast(int, s2a), 0x4E, 0xF, 0xF, false));   // quad_perm(2,3,0,1)
-                        const float r2b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                            __builtin_bit_cast(int, s2b), 0x4E, 0xF, 0xF, false));
-                        if (upper) { v0 = r2a; v1 = r2b; } else { v2 = r2a; v3 = r2b; }
-                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + 4 * (l32 >> 2);
-                        if (local < row_count && col < N)   // N % 16 == 0: four columns are in or out together
-                            *reinterpret_cast<float4_t*>(p.out_f32 + (row_start + local) * N + col) =
-                                (float4_t){v0, v1, v2, v3};
-                    }
-                }
-            }
+            store_f32(p.out_f32, alpha);
+        } else if (p.ksplit > 1) {
+            store_f32(p.partial + (int64_t)chunk * p.M * N, 1.0f);
         } else {
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
@@ -560,8 +587,7 @@ void gemm_kernel(GemmParams p) {
                         const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + l32;
                         if (col >= N) continue;
                         const float v = alpha * acc[i][j][r];
-                        if (MODE == kGemmL2) p.out_f32[prow * N + col] = v;
-                        else p.out_bf16[prow * N + col] = (uint16_t)f32_to_bf16_rne(v);
+                        p.out_bf16[prow * N + col] = (uint16_t)f32_to_bf16_rne(v);
                     }
                 }
             }
@@ -577,7 +603,8 @@ template <int MODE>
 hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     const int64_t ntn = (MODE == kGemmL1) ? (p.I + 127) / 128 : (p.N + BN - 1) / BN;
     const int64_t mt = (MODE == kGemmDense) ? (p.M + BM - 1) / BM : p.max_tiles;
-    const int64_t grid = (mt + 7) / 8 * 8 * ntn;     // whole groups of 8 tiles (one per XCD)
+    // grouped: whole groups of 8 tiles (one per XCD); dense: every (tile, N-tile, K chunk)
+    const int64_t grid = (MODE == kGemmDense) ? mt * ntn * p.ksplit : (mt + 7) / 8 * 8 * ntn;
     if (grid <= 0) return hipSuccess;
     static std::atomic<int> lds_set[kMaxDevices];
     hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(&gemm_kernel<MODE>), LDS_BYTES, lds_set);
@@ -586,7 +613,63 @@ hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// One thread per 4 columns of one row: the chunks' partial sums in chunk
+// order, times alpha, rounded once to bf16.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial, int ksplit,
+                                                            int64_t M, int64_t N, const float* __restrict__ a_gs,
+                                                            const float* __restrict__ b_alpha,
+                                                            uint16_t* __restrict__ out) {
+    const float alpha = a_gs[0] * b_alpha[0];
+    const int64_t n4 = M * N / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const float* src = partial + 4 * i;
+        float4_t acc = *reinterpret_cast<const float4_t*>(src);
+        // loads in batches of 8 chunks, all in flight before the first add
+        for (int c0 = 1; c0 < ksplit; c0 += 8) {
+            float4_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (c0 + j < ksplit) v[j] = *reinterpret_cast<const float4_t*>(src + (int64_t)(c0 + j) * M * N);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (c0 + j < ksplit) {
+                    acc[0] = acc[0] + v[j][0];
+                    acc[1] = acc[1] + v[j][1];
+                    acc[2] = acc[2] + v[j][2];
+                    acc[3] = acc[3] + v[j][3];
+                }
+        }
+        u32x2 o;
+        o[0] = f32_to_bf16_rne(alpha * acc[0]) | (f32_to_bf16_rne(alpha * acc[1]) << 16);
+        o[1] = f32_to_bf16_rne(alpha * acc[2]) | (f32_to_bf16_rne(alpha * acc[3]) << 16);
+        *reinterpret_cast<u32x2*>(out + 4 * i) = o;
+    }
+}
+
 }  // namespace
+
+int dense_ksplit(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = (M + BM - 1) / BM * ((N + BN - 1) / BN);
+    const int64_t nk = pitch_q(K) / 32;
+    if (tiles <= 0 || tiles >= 128 || nk < 8) return 1;
+    // at most one work-group per CU: a second round would double the time
+    int64_t s = 256 / tiles;
+    if (s > nk / 4) s = nk / 4;
+    if (s < 1) s = 1;
+    // chunks of ceil(nk / s) steps; as many as that length needs, so that
+    // none is empty
+    const int64_t per = (nk + s - 1) / s;
+    return (int)((nk + per - 1) / per);
+}
+
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const float* a_gs,
+                                const float* b_alpha, uint16_t* out, hipStream_t s) {
+    const int64_t n4 = M * N / 4;
+    if (n4 <= 0) return hipSuccess;
+    const int64_t g = (n4 + 255) / 256;
+    splitk_reduce_kernel<<<(unsigned)(g < 4096 ? g : 4096), 256, 0, s>>>(partial, ksplit, M, N, a_gs, b_alpha, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     // 32-bit buffer offsets: every operand must stay below 2 GiB

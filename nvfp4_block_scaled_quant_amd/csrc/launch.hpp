@@ -208,9 +208,24 @@ struct GemmParams {
     int64_t I;                 // L1: act columns (N = 2I)
     uint32_t* amax_slot;       // L1: act amax (atomic max of float bits)
     uint16_t* gu_tap;          // L1: null, or (rows, 2I) bf16 gate | up values out
+    // dense with ksplit > 1: the K steps are cut into ksplit chunks, each
+    // summed by its own work-groups into partial[chunk] (M, N) float32 (no
+    // alpha); launch_splitk_reduce then forms out_bf16
+    int ksplit;
+    float* partial;
 };
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+// Number of K chunks of the dense GEMM: 1 when its tiles fill half the GPU,
+// else as many as keep (tiles x chunks) within one work-group per CU, each
+// chunk at least 4 K steps and none empty.
+int dense_ksplit(int64_t M, int64_t N, int64_t K);
+
+// out[m][n] = bf16((a_gs[0] * b_alpha[0]) * sum over chunks c, in order, of
+// partial[c][m][n]) for (M, N), N % 4 == 0.
+hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const float* a_gs,
+                                const float* b_alpha, uint16_t* out, hipStream_t s);
 
 // Weight-streaming variant for tiles of at most kSkinnyBM rows (L1 / L2 only).
 // It stages the tile's A rows whole in LDS: skinny_lds_bytes(K) must not

@@ -106,14 +106,15 @@ __global__ __launch_bounds__(kThreads) void dequant_rows_f16_kernel(const uint8_
                                                                     const uint8_t* __restrict__ sf,
                                                                     int64_t M, int64_t K,
                                                                     uint8_t* __restrict__ h) {
-    const int64_t groups = K / 16, ldh = pitch_h(K);
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < M * groups;
-         b += (int64_t)gridDim.x * kThreads) {
-        const int64_t r = b / groups, g = b - r * groups;
+    // 32-bit index arithmetic: callers keep M * pitch_h(K) (> 32 M * K / 16) below 2^31
+    const uint32_t groups = (uint32_t)(K / 16), ldh = (uint32_t)pitch_h(K);
+    const uint32_t total = (uint32_t)M * groups;
+    for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
+        const uint32_t r = b / groups, g = b - r * groups;
         const u32x2 w = *reinterpret_cast<const u32x2*>(q + b * 8);
         store_block_f16(h + r * ldh + g * 32, w[0], w[1], sf[b]);
         if (g == groups - 1)
-            for (int64_t j = groups * 32; j < ldh; j += 16)
+            for (uint32_t j = groups * 32; j < ldh; j += 16)
                 *reinterpret_cast<u32x4*>(h + r * ldh + j) = (u32x4){0u, 0u, 0u, 0u};
     }
 }

@@ -73,3 +73,29 @@ def test_noalloc_rejects_oversized_problem(nv):
         nv.moe_forward_noalloc(x, ids, wts, pw["w13"], pw["w13_sf"], pw["w13a"], pw["w2"], pw["w2_sf"],
                                pw["w2a"])
     assert e.value.status == 6
+
+
+def test_noalloc_in_a_hip_graph(nv):
+    # the use it is for: the layer captured into a HIP graph (no allocation or
+    # workspace inside the captured call). Every replay, with eager calls and
+    # synchronizations between them, must give the eager result bit for bit.
+    import torch
+    for cfg in (W.small_layer("nag1", T=6, H=256, I=128, E=4, topk=2, seed=36),
+                W.small_layer("nag2", T=120, H=256, I=128, E=4, topk=2, seed=37)):
+        L, pw, d = _layer(nv, cfg)
+        args = (d["x"], d["ids"], d["wts"], pw["w13"], pw["w13_sf"], pw["w13a"], pw["w2"], pw["w2_sf"],
+                pw["w2a"])
+        y_ref = to_host(nv.moe_forward(*args))
+        y = torch.empty_like(d["x"])
+        nv.moe_forward_noalloc(*args, y=y)          # first call on the device: set-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            nv.moe_forward_noalloc(*args, y=y)
+        for rep in range(3):
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert (to_host(y) == y_ref).all(), f"{cfg.name}: replay {rep} differs"
+            assert (to_host(nv.moe_forward(*args)) == y_ref).all()     # eager work between replays
+            torch.cuda.synchronize()
