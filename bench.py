@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode batch (profiling runs)")
-    ap.add_argument("--only", choices=("prefill", "skewed", "dense", "decode"), default=None,
+    ap.add_argument("--only", choices=("prefill", "skewed", "dense", "decode", "vendor-gemm"), default=None,
                     help="run one measurement and print its JSON (profiling runs)")
     ap.add_argument("--no-graph", action="store_true", help="decode: skip the HIP-graph timing")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -373,6 +373,31 @@ def calibrate_copy():
         del a, b
 
 
+def vendor_f16_gemm(n=8192, reps=20):
+    """torch.matmul (hipBLASLt) on contiguous n x n x n f16 operands: what the
+    vendor's own f16 GEMM reaches on this GPU at the clock the chip holds
+    under full MFMA load. Context for the L1/L2 fractions, not the peak."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
+    c = torch.empty((n, n), device="cuda", dtype=torch.float16)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    tf = 2.0 * n ** 3 / (us * 1e-6) / 1e12
+    del a, b, c
+    return {"shape": f"{n} x {n} x {n} f16, f32 accumulate", "us_per_call": us, "tflops": tf,
+            "f16_peak_frac": tf / PEAK_F16_MFMA_TFLOPS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +410,9 @@ def main():
         sys.exit(1)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.only == "vendor-gemm":
+        print(json.dumps(vendor_f16_gemm()), flush=True)
         return
     import nvfp4_block_scaled_quant_amd as nv
     import workloads as W
@@ -459,6 +487,7 @@ def main():
     # the other configurations of the workload recipe, each measured the same way
     out["skewed"] = time_skewed(nv, weights, max(5, args.steps // 2), 2)
     out["dense_gemm"] = time_dense_gemm(nv)
+    out["vendor_f16_gemm"] = vendor_f16_gemm()
     if not args.no_decode:
         out["decode"] = time_decode(nv, weights, args.decode_steps)
     del weights

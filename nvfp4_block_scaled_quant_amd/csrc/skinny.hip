@@ -5,17 +5,17 @@
 // With a handful of rows per expert the layer is bound by reading the expert
 // weights from HBM once, so the kernel is built around the weight stream:
 //
-// * A work-group owns one 16-row tile and a slab of 4 x 128 weight rows
-//   (output columns; for L1: 4 x 64 gate columns and the matching up
-//   columns). Its 16 A rows are staged once in LDS, still packed, while the
+// * A work-group owns one 16-row tile and a slab of 4 x 16 NB weight rows
+//   (output columns; NB = 10 for L2; for L1, NB = 8: 4 x 64 gate columns and
+//   the matching up columns). Its 16 A rows are staged once in LDS, still packed, while the
 //   first weight loads are already in flight.
-// * Each wave streams its own 128 weight rows over the whole of K, two K
+// * Each wave streams its own 16 NB weight rows over the whole of K, two K
 //   steps in flight, with non-temporal loads (the weights are read once),
 //   and finishes its outputs by itself (no cross-wave reduction). Per
 //   128-element K step, lane (c, q) = (lane % 16, lane / 16) loads 16
 //   contiguous bytes (32 K values, [32q, 32q + 32) of the step) from each of
-//   8 weight rows: column c of the 8 MFMA column blocks f (block f
-//   holds weight rows 16f + c of the wave's 128). In the packed weight layout
+//   NB weight rows: column c of the NB MFMA column blocks f (block f
+//   holds weight rows 16f + c of the wave's 16 NB). In the packed weight layout
 //   one such load instruction (16 rows x 64 bytes of one K step of a 16-row
 //   block, stored as two half steps of 16 x 32 bytes) reads one contiguous
 //   kilobyte.
@@ -46,9 +46,13 @@ namespace {
 constexpr int NT = 256;
 constexpr int NW = NT / 64;       // waves per work-group
 constexpr int SM = 16;            // rows per tile
-constexpr int NB = 8;             // MFMA column blocks per lane (weight rows 16f + c)
-constexpr int WROWS = 16 * NB;    // weight rows per wave
-constexpr int GB = NB / 2;        // L1: gate blocks (and as many up blocks) per wave
+// MFMA column blocks per lane (weight rows 16f + c of the wave's 16 * NB):
+// L1 4 gate + 4 up blocks; L2 10 blocks, so that a tile needs 12 work-groups
+// for 7168 output columns instead of 14 at 8 blocks: the decode batch touches
+// up to about 42 experts, and 42 x 12 work-groups still fit the 512 that the
+// GPU holds at once (two per CU), where 37 x 14 already need a second round
+// whose few work-groups each take a whole stream's latency-bound time
+template <int MODE> constexpr int kNB = MODE == kGemmL1 ? 8 : 10;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr int kStreamNT = 2;      // buffer-load cache policy: non-temporal (read once)
 constexpr int kStagger = 13;      // start offset (in groups of four K steps) between waves
@@ -58,14 +62,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
 }
 
-// work-group slabs per tile: L1 in act columns (16 * GB per wave), L2 in rows
+// work-group slabs per tile: L1 in act columns (16 * NB / 2 per wave), L2 in rows (16 * NB)
 __host__ __device__ inline int64_t skinny_slabs(int mode, int64_t I, int64_t N) {
-    return mode == kGemmL1 ? (I + NW * 16 * GB - 1) / (NW * 16 * GB) : (N + NW * WROWS - 1) / (NW * WROWS);
+    constexpr int c1 = NW * 16 * (kNB<kGemmL1> / 2), c2 = NW * 16 * kNB<kGemmL2>;
+    return mode == kGemmL1 ? (I + c1 - 1) / c1 : (N + c2 - 1) / c2;
 }
 
 template <int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void skinny_kernel(GemmParams p) {
+    constexpr int NB = kNB<MODE>;
+    constexpr int WROWS = 16 * NB;    // weight rows per wave
+    constexpr int GB = NB / 2;        // L1: gate blocks (and as many up blocks) per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
