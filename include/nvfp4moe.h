@@ -2,7 +2,7 @@
  * nvfp4moe.h - C ABI of the NVFP4 mixture-of-experts expert layer for AMD
  * Instinct MI355X (gfx950).
  *
- * Formats (the pages: "nvfp4-megamoe-kernel" DEBUG_LOG, the "NVFP4 MoE
+ * Formats (the pages: the NVFP4 MegaMoE Debug Log of nvfp4-megamoe-kernel, the "NVFP4 MoE
  * Pipeline" and Hypotheses 2, 3, 5, 6; its later revision's "input_scale red
  * herring" and code-review items; the src commit log's quantizer, E4M3 and
  * gate/up fixes):
@@ -123,7 +123,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K,
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_quantize_static - stage_activation with a global scale given by the
- * caller instead of amax / 2688 of x (the later DEBUG_LOG revision, "input_scale
+ * caller instead of amax / 2688 of x (the later revision of the NVFP4 MegaMoE Debug Log, "input_scale
  * red herring": a calibrated activation scale in that role; the pages found
  * the checkpoint's calibrated value unsuitable for their runtime data, so the
  * scale is entirely the caller's choice). Saves the amax pass.
@@ -142,7 +142,7 @@ int nvfp4_quantize_static(const uint16_t* x, int64_t M, int64_t K, const float* 
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_quantize_weights - the loader's rule for a batch of E weight
- * matrices (DEBUG_LOG, Hypothesis 6 steps 1-5): per matrix one global scale,
+ * matrices (NVFP4 MegaMoE Debug Log, Hypothesis 6 steps 1-5): per matrix one global scale,
  * blocks of 16 along K, output in the K-packed weight layout.
  *
  *   w        (E, K, N) bf16, W[e] is the math layout (y = x @ W[e]), K % 16 == 0
@@ -162,7 +162,7 @@ int nvfp4_quantize_weights(const uint16_t* w, int64_t E, int64_t K, int64_t N,
  * column part: W[e] (K, N) is split along N into `parts` equal ranges and
  * each range is quantized as its own matrix (own amax, own alpha). For w13 =
  * [gate | up] with parts = 2 these are the per-half weight global scales of
- * the DEBUG_LOG ("Bugs Fixed": a global scale of shape (2,) applied per half;
+ * the NVFP4 MegaMoE Debug Log ("Bugs Fixed": a global scale of shape (2,) applied per half;
  * later revision, code-review item 5: a per-column alpha), which the layer
  * takes through nvfp4_moe_options.w13_alpha_per_half.
  *
@@ -202,7 +202,7 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_gemm - block-scaled NVFP4 GEMM, one expert
- * (DEBUG_LOG, "NVFP4 MoE Pipeline": GEMM with alpha = igs * weight global).
+ * (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline": GEMM with alpha = igs * weight global).
  *
  *   out[m][n] = bf16( (a_gs[0] * b_alpha[0]) * sum_k deqA[m][k] * deqB[k][n] )
  *
@@ -233,7 +233,7 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_moe_forward - the five-stage NVFP4 expert layer on one GPU's experts
- * (DEBUG_LOG, "NVFP4 MoE Pipeline"):
+ * (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline"):
  *   1. quantize x (T, H) -> xq, xsf, gs1 (nvfp4_quantize's rule, one gs1 over x)
  *   2. route: one slot per (t, j) whose id topk_ids[t][j] is in [0, E);
  *      slots with other ids are skipped and contribute nothing
@@ -388,9 +388,9 @@ int nvfp4_moe_forward_noalloc(const uint16_t* x, const int32_t* topk_ids, const 
 
 /* ------------------------------------------------------------------------ *
  * nvfp4_route_topk - the router that produces the layer's topk_ids and
- * topk_weights (the routing weights of the DEBUG_LOG's final "scatter with
- * routing weights"; the pages do not define the router, this is the usual
- * top-k with renormalized softmax):
+ * topk_weights (the weights of the routing-weighted scatter that ends the
+ * NVFP4 MegaMoE Debug Log's "NVFP4 MoE Pipeline"; the pages do not define the
+ * router, this is the usual top-k with renormalized softmax):
  *
  *   logits        (T, E) float32, finite
  *   topk_ids      (T, topk) int32 out: the topk largest logits of each row in

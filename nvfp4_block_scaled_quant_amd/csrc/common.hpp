@@ -3,7 +3,7 @@
 // Number formats follow the "nvfp4-megamoe-kernel" pages: E2M1 nibbles are
 // sign-magnitude (bit 3 sign, bits 2:0 index {0,.5,1,1.5,2,3,4,6}), two per
 // byte with the even element low; scale bytes are OCP E4M3FN bit patterns
-// (bias 7, max 448) per 16 elements (DEBUG_LOG Hypothesis 5/6, src commit log
+// (bias 7, max 448) per 16 elements (NVFP4 MegaMoE Debug Log Hypothesis 5/6, src commit log
 // quantizer and `.view` fixes).
 #pragma once
 

@@ -1,5 +1,5 @@
 // Block-scaled NVFP4 GEMMs on gfx950 matrix cores: the dense GEMM and the two
-// grouped GEMMs of the expert layer (DEBUG_LOG, "NVFP4 MoE Pipeline": L1 with
+// grouped GEMMs of the expert layer (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline": L1 with
 // alpha = igs * l1_global_sf, SiLU(gate) * up, L2 with alpha = l1_igs *
 // l2_global_sf; Hypothesis 3: alphas stay out of the E4M3 scales).
 //
@@ -47,7 +47,12 @@
 // come from a device-built list (expert, first sorted row, row count) with
 // all full tiles before the partial ones; the grid is sized for the worst
 // case and idle work-groups leave at once, so the host never waits for
-// routing counts. Invalid rows and columns of a tile read a valid row instead
+// routing counts. The dense GEMM has no tile list and few tiles (a 256-row
+// M is 24 tiles at N = 6144): its work-groups go in plain order, and when its
+// tiles would fill less than half the GPU the K steps are cut into chunks, one
+// work-group per (tile, chunk) with at most one work-group per CU, each
+// writing float32 partial sums that a second kernel adds in chunk order
+// before the one bf16 rounding. Invalid rows and columns of a tile read a valid row instead
 // (their results are never stored). Rows are read in whole steps: the padding
 // of a partial last step is zero in both operands (the quantizers and the
 // weight prepack write it as zeros), so it adds nothing.

@@ -1,6 +1,6 @@
 // NVFP4 dynamic quantization kernels (gfx950).
 //
-// The rule is the pages' stage_activation / weight-loader rule (DEBUG_LOG,
+// The rule is the pages' stage_activation / weight-loader rule (NVFP4 MegaMoE Debug Log,
 // Hypothesis 6 steps 1-5; "NVFP4 MoE Pipeline"): global scale amax/(6*448) over
 // the whole tensor, E4M3 block scale block_amax/(6*global) per 16 elements,
 // nearest E2M1, even element in the low nibble. The arithmetic order is fixed

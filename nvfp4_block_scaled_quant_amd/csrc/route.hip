@@ -1,8 +1,8 @@
 // Token-to-expert permutation and the routing-weighted combine (gfx950).
 //
-// The pages name the permutation ("slots", "slot_token") and the final
-// "scatter with routing weights" (DEBUG_LOG, "Pipeline Trace" and "NVFP4 MoE
-// Pipeline") without defining them. The reading implemented here: one slot per
+// The pages name the permutation (slots, slot_token) and the final
+// routing-weighted scatter (NVFP4 MegaMoE Debug Log, "Pipeline Trace" and
+// "NVFP4 MoE Pipeline") without defining them. The reading implemented here: one slot per
 // (token t, choice j), s = t * topk + j, whose expert id is in [0, E); slots
 // are sorted by expert, stably by slot index, so every expert's rows form one
 // contiguous range of the "sorted row" order the grouped GEMMs walk; slots with
@@ -10,12 +10,15 @@
 // topk_weights[t][j] times the L2 row of slot (t, j), float32, then one bf16
 // rounding.
 //
-// Routing runs in a single 1024-thread work-group: it is a few microseconds of
-// integer work on at most a few tens of thousands of slots and it produces the
-// whole tile list on the device, so the host never waits for counts. For a
-// small batch further work-groups of the same launch quantize the layer input
-// (each takes the amax of the whole input, then does its share of the block
-// pass), saving two launches.
+// Routing is a few microseconds of integer work and produces the whole tile
+// list on the device, so the host never waits for counts. A small batch is
+// routed by one 1024-thread work-group; a large one in chunks of 4,096 slots,
+// one work-group each, after a pre-pass that counts every chunk's expert ids
+// (each routing work-group then knows the global counts and where its chunk's
+// rows of every expert start, and scatters its chunk stably). Further
+// work-groups of the same launch quantize the layer input, saving launches:
+// for a small batch each takes the amax of the whole input itself, for a
+// large one the pre-pass's partial maxima.
 #include "common.hpp"
 #include "launch.hpp"
 

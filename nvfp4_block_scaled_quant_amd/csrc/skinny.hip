@@ -1,5 +1,5 @@
 // Weight-streaming grouped GEMMs for small batches (decode): the same two
-// expert GEMMs as gemm.hip (DEBUG_LOG, "NVFP4 MoE Pipeline", L1 with fused
+// expert GEMMs as gemm.hip (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline", L1 with fused
 // SiLU(gate) * up and L2), for tiles of at most 16 rows.
 //
 // With a handful of rows per expert the layer is bound by reading the expert

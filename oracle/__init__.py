@@ -17,13 +17,13 @@ pages; sections named there):
 * ``quantize``  the two-level NVFP4 quantization of a tensor: global scale
                 amax/(6*448), one E4M3 scale per 16 elements equal to
                 block_amax/(6*global), nearest E2M1 value, two nibbles per byte
-                with the even element in the low nibble (DEBUG_LOG, Hypothesis 6
+                with the even element in the low nibble (NVFP4 MegaMoE Debug Log, Hypothesis 6
                 "vLLM weight loader" steps 1-5; Hypothesis 5 packing; later
                 revision, "input_scale red herring" and code-review item 1).
 * ``gemm``      dequantization and the block-scaled GEMM with the per-expert
-                fp32 alpha applied outside the E4M3 scales (DEBUG_LOG,
+                fp32 alpha applied outside the E4M3 scales (NVFP4 MegaMoE Debug Log,
                 Hypothesis 3 and "NVFP4 MoE Pipeline"), accumulated in fp64.
-* ``moe``       the five-stage expert layer of DEBUG_LOG "NVFP4 MoE Pipeline".
+* ``moe``       the five-stage expert layer of the NVFP4 MegaMoE Debug Log "NVFP4 MoE Pipeline".
 * ``loops``     an independent pure-Python twin (exact rational arithmetic)
                 used only on tiny shapes to pin the vectorized code.
 

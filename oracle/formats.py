@@ -4,8 +4,8 @@
   significant bits, 8 exponent bits, bias 127).
 * E4M3FN (OCP FP8): 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
   infinities, NaN at S.1111.111, largest finite 448. The pages' global scale
-  amax/(6*448) names this 448 (DEBUG_LOG revision, "input_scale red herring";
-  DEBUG_LOG, Hypothesis 6 step 2). Scale bytes are bit patterns of this format:
+  amax/(6*448) names this 448 (NVFP4 MegaMoE Debug Log, later revision, "input_scale red herring";
+  NVFP4 MegaMoE Debug Log, Hypothesis 6 step 2). Scale bytes are bit patterns of this format:
   a stored byte is reinterpreted, never converted by value (src commit log,
   fix of the E4M3 unpack that used `.to` where `.view` was needed).
 * E2M1 (FP4): sign-magnitude nibble, bit 3 the sign, bits 2:0 an index into the

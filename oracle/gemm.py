@@ -4,11 +4,11 @@ C = (gs_A * alpha_B) * deq(A) @ deq(B), every product of an E2M1 value and an
 E4M3 scale exact, accumulated in float64 and left unrounded.
 
 The per-tensor / per-expert fp32 scales enter only as the GEMM's alpha and are
-never folded into the E4M3 block scales (DEBUG_LOG, Hypothesis 3; src commit
+never folded into the E4M3 block scales (NVFP4 MegaMoE Debug Log, Hypothesis 3; src commit
 log, per-expert global scale fix); the activation's global scale times the
-weight's global scale is that alpha (DEBUG_LOG, "NVFP4 MoE Pipeline": L1 and L2
+weight's global scale is that alpha (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline": L1 and L2
 GEMM lines). A is row-major with K packed along its rows; B is (K/2, N) packed
-along K (DEBUG_LOG, Hypothesis 2 shapes; Hypothesis 5 packing).
+along K (NVFP4 MegaMoE Debug Log, Hypothesis 2 shapes; Hypothesis 5 packing).
 
 Parity pins (tests/test_oracle_gemm.py): exact-rational brute force on tiny
 shapes (oracle.loops), single-scale probes that move only their own row or

@@ -1,6 +1,6 @@
 """The five-stage NVFP4 mixture-of-experts expert layer (test infrastructure).
 
-Stages as the pages list them (DEBUG_LOG, "NVFP4 MoE Pipeline"):
+Stages as the pages list them (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline"):
 
 1. ``stage_activation(hidden)``: quantize x with the NVFP4 rule (oracle.quantize),
    one global scale gs1 over all of x;
@@ -12,7 +12,8 @@ Stages as the pages list them (DEBUG_LOG, "NVFP4 MoE Pipeline"):
    (src commit log, gate/up interleave removal);
 4. act = SiLU(gate) * up, then ``stage_activation(act)``: one global scale gs2
    over the activations of all valid slots;
-5. L2 GEMM with alpha = gs2 * w2_alpha[e], then "scatter with routing weights":
+5. L2 GEMM with alpha = gs2 * w2_alpha[e], then the routing-weighted scatter
+   of the L2 rows back to their tokens:
    y[t] = sum_j topk_weights[t, j] * out[t, j] in j order.
 
 Rounding points (the pages print bf16-looking intermediates and say "bf16 out";

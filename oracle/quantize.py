@@ -1,8 +1,8 @@
 """NVFP4 two-level quantization and dequantization (test infrastructure).
 
 Follows the rule the pages give for the weight loader and for
-``stage_activation`` (DEBUG_LOG, Hypothesis 6 steps 1-5 and "NVFP4 MoE
-Pipeline"; DEBUG_LOG revision, "input_scale red herring"; src commit log,
+``stage_activation`` (NVFP4 MegaMoE Debug Log, Hypothesis 6 steps 1-5 and "NVFP4 MoE
+Pipeline"; NVFP4 MegaMoE Debug Log, later revision, "input_scale red herring"; src commit log,
 quantizer fix and E4M3 `.view` fix):
 
 1. global scale  gs = amax / (6 * 448), amax over the whole tensor;
@@ -18,8 +18,9 @@ every GPU path must follow the same one (the readings are listed in the design doc):
   in exactly this order: gs = fl(amax / 2688); six_gs = fl(6 * gs);
   s = fl(bmax / six_gs), clamped to 448; den = fl(s_stored * gs);
   v = fl(|x| / den);
-* the element divides by the *stored* (decoded) block scale: the stored byte is
-  "the actual dequant factor" (src commit log, quantizer fix item 2);
+* the element divides by the *stored* (decoded) block scale, the byte that
+  dequantization will multiply by (the nvfp4-megamoe-kernel src commit log,
+  quantizer fix, item 2, which calls the stored block_max/6 the dequant factor);
 * gs == 0 gives scale 0; den == 0 gives magnitude 0;
 * the nibble's sign bit is the sign bit of x, also for -0.0 and for negative
   values that round to magnitude 0.
@@ -68,7 +69,7 @@ def quantize_f32_static(x, gs):
     """Steps 2-4 of the rule with a global scale given by the caller.
 
     The static variant of stage_activation: gs is a fixed (e.g. calibrated)
-    activation scale instead of amax / 2688 of this tensor (the later DEBUG_LOG
+    activation scale instead of amax / 2688 of this tensor (the later NVFP4 MegaMoE Debug Log
     revision discusses the checkpoint's calibrated ``input_scale`` in that
     role). Nothing else changes: a block whose amax exceeds 6 * 448 * gs gets
     the largest scale (s is clamped to 448, byte 0x7E) and its elements
@@ -139,7 +140,7 @@ def quantize_weight_bf16_parts(w_bits, parts):
     W (K, N) is split along N into `parts` equal column ranges; each range is
     quantized with the weight rule on its own (its own amax), and the results
     are concatenated back along N. For w13 = [gate | up] with parts = 2 this is
-    the per-half weight global scale of the DEBUG_LOG ("Bugs Fixed", BF16
+    the per-half weight global scale of the NVFP4 MegaMoE Debug Log ("Bugs Fixed", BF16
     reference item 4: a global scale of shape (2,), applied per half) and of
     the later revision's code-review item 5 (scaling the up half by the ratio
     of the halves' scales is a per-column alpha).

@@ -1,7 +1,8 @@
 """Top-k router with renormalized softmax weights (test infrastructure).
 
-The layer's inputs topk_ids / topk_weights are what the final "scatter with
-routing weights" of the DEBUG_LOG ("NVFP4 MoE Pipeline") consumes. The pages
+The layer's inputs topk_ids / topk_weights are what the last stage of the
+NVFP4 MegaMoE Debug Log's "NVFP4 MoE Pipeline" (the routing-weighted scatter
+of the L2 rows) consumes. The pages
 do not define how they are produced; the reading taken (the plainest one, and
 the one the synthetic workloads use) is the usual MoE router on per-token
 logits over the E local experts:

@@ -101,7 +101,7 @@ def test_gemm_single_scale_probes(nv):
 
 
 def test_gemm_one_hot_k_probes_at_real_shape(nv):
-    # DEBUG_LOG Hypothesis 8: the probes passed at test shapes but the real shape
+    # NVFP4 MegaMoE Debug Log Hypothesis 8: the probes passed at test shapes but the real shape
     # M=1, N=6144, K=7168 was never probed. One-hot A rows read single K rows of
     # deq(B) (checks B's nibble order independently of A's) at that shape.
     rng = np.random.default_rng(3)

@@ -43,9 +43,10 @@ def tiny():
 
 
 def test_vectorized_layer_matches_exact_twin_on_tiny_config(tiny):
-    # "A wrong reference is worse than no reference" (DEBUG_LOG revision): the
-    # NumPy oracle must agree bit for bit with the exact-rational twin before it
-    # is trusted against any GPU result
+    # The pages' later revision of the NVFP4 MegaMoE Debug Log (its status line
+    # and the note on the 0.2-cosine reference) found that a faulty reference
+    # had cost them many iterations: the NumPy oracle must agree bit for bit
+    # with the exact-rational twin before it is trusted against any GPU result
     L = tiny
     t0 = time.time()
     ref = run(L)
@@ -129,7 +130,7 @@ def test_skipped_slots(tiny):
 
 
 def test_combine_is_weighted_sum_of_l2_rows(tiny):
-    # "scatter with routing weights": y[t] = sum_j w[t,j] * out[t,j]
+    # the routing-weighted scatter of stage 5: y[t] = sum_j w[t,j] * out[t,j]
     L = tiny
     out = run(L)
     assert np.allclose(out["y"], out["contrib"].sum(axis=1), rtol=1e-14, atol=0)

@@ -19,7 +19,7 @@ def _rand_bits(rng, shape, std=3.0):
 
 
 def test_global_scale_pairs_printed_on_pages():
-    # DEBUG_LOG "Symptoms" (amax 3.86 -> igs 1.4e-3) and the later revision's
+    # NVFP4 MegaMoE Debug Log "Symptoms" (amax 3.86 -> igs 1.4e-3) and the later revision's
     # calibration arithmetic (2.86e-4 * 6 * 448 = 0.77)
     for amax, printed, digits in read_golden("global_scale_pairs.txt"):
         gs = float(global_scale(np.float32(float(amax))))
@@ -161,7 +161,7 @@ def test_e4m3_midpoints_through_the_quantizer_match_twin():
 
 def test_unpack_is_inverse_of_pack_nonsquare():
     # unpack along K for a (K/2, N) tensor with K/2 != N; the pages' reshape bug
-    # (DEBUG_LOG, "Weight nibble unpack reshape bug") interleaved along N instead
+    # (NVFP4 MegaMoE Debug Log, "Weight nibble unpack reshape bug") interleaved along N instead
     rng = np.random.default_rng(17)
     nib = rng.integers(0, 16, size=(12, 5)).astype(np.uint8)     # (K, N)
     packed = nib[0::2] | (nib[1::2] << 4)                        # (K/2, N)
