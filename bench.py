@@ -52,12 +52,13 @@ def parse():
 
 
 def gemm_source_hash():
-    """Hash of the GEMM kernel's sources with comments and blank space removed:
+    """Hash of the GEMM kernel's sources (and of the routing kernel, which
+    orders its tiles) with comments and blank space removed:
     the stored PMC traffic is reported only while this matches, i.e. until the
     code (not its commentary) changes."""
     import re
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp", "launch.hpp"):
+    for f in ("gemm.hip", "common.hpp", "launch.hpp", "route.hip"):     # route.hip: the tile order
         with open(os.path.join(ROOT, "nvfp4_block_scaled_quant_amd", "csrc", f)) as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)

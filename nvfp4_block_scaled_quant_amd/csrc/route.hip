@@ -147,8 +147,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t* off = cnt + E;                          // global first sorted row per expert
     int32_t* gbase = off + E + 1;                    // this chunk's first row per expert, past off
     int32_t* wcnt = gbase + E;                       // [kWaves][E]: counts, then running positions
-    __shared__ int32_t tile_base[kMaxExperts + 1];   // first full tile of each expert
-    __shared__ int32_t part_base[kMaxExperts + 1];   // its partial tile (after all full ones)
+    __shared__ int32_t tile_base[kMaxExperts + 1];   // first tile of each expert
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -210,37 +209,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
 
-    // exclusive scans of counts, of full tiles and of partial tiles per expert:
-    // wave 0, 64 experts at a time, shuffle-based inclusive scans within the
-    // wave. The tile list holds every expert's full BM-row tiles first and the
-    // partial tiles (fewer rows, less work) after them: the grouped GEMM's
-    // last round of work-groups then consists of the short ones.
+    // exclusive scans of counts and of tiles per expert: wave 0, 64 experts
+    // at a time, shuffle-based inclusive scans within the wave. The tile list
+    // holds the experts in order, each with its full BM-row tiles and then its
+    // partial one. So every round of GEMM work-groups mixes full and partial
+    // (shorter) tiles, and the rounds drift apart: the work-groups do not all
+    // store their results and load their next tiles at the same moment, which
+    // measured 2-3% faster on both grouped GEMMs than all full tiles first
+    // (one long round of equal tiles after another).
     if (wave == 0) {
-        int acc = 0, facc = 0, pacc = 0;
+        int acc = 0, tacc = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int c = (e < E) ? cnt[e] : 0;
-            const int f = c / BM, q = (c % BM) ? 1 : 0;
-            int ic = c, jf = f, jq = q;
+            const int nt = (c + BM - 1) / BM;
+            int ic = c, jt = nt;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                const int uc = __shfl_up(ic, d), uf = __shfl_up(jf, d), uq = __shfl_up(jq, d);
-                if (lane >= d) { ic += uc; jf += uf; jq += uq; }
+                const int uc = __shfl_up(ic, d), ut = __shfl_up(jt, d);
+                if (lane >= d) { ic += uc; jt += ut; }
             }
             if (e < E) {
                 off[e] = acc + ic - c;
-                tile_base[e] = facc + jf - f;
-                part_base[e] = pacc + jq - q;
+                tile_base[e] = tacc + jt - nt;
             }
             acc += __shfl(ic, 63);
-            facc += __shfl(jf, 63);
-            pacc += __shfl(jq, 63);
+            tacc += __shfl(jt, 63);
         }
         if (lane == 0) {
             off[E] = acc;
-            tile_base[E] = facc;         // number of full tiles
-            part_base[E] = pacc;
-            if (g == 0) *num_tiles = facc + pacc;
+            tile_base[E] = tacc;
+            if (g == 0) *num_tiles = tacc;
         }
     }
     __syncthreads();
@@ -248,15 +247,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         for (int e = tid; e <= E; e += kRouteThreads) offsets[e] = off[e];
         for (int e = tid; e < E; e += kRouteThreads) {
             counts[e] = cnt[e];
-            const int nf = cnt[e] / BM;
-            for (int i = 0; i <= nf; ++i) {
+            const int nt = (cnt[e] + BM - 1) / BM;
+            for (int i = 0; i < nt; ++i) {
                 Tile t;
                 t.expert = e;
                 t.row_start = off[e] + i * BM;
                 t.row_count = min(BM, cnt[e] - i * BM);
                 t.pad = 0;
-                if (i < nf) tiles[tile_base[e] + i] = t;
-                else if (t.row_count > 0) tiles[tile_base[E] + part_base[e]] = t;
+                tiles[tile_base[e] + i] = t;
             }
         }
     }
