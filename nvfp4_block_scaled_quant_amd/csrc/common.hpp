@@ -128,14 +128,16 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u, bool& ok) {
 }
 
 // The lanes of the wave whose (g, v) silu_f32_decides rejects, as a mask:
-// one ballot per condition, so each is the compare's own lane mask.
+// one ballot per condition, so each is the compare's own lane mask. "v not
+// normal" is one class test for the classes NaN (signaling 1, quiet 2),
+// -inf (4), -subnormal (16), -0 (32), +0 (64), +subnormal (128), +inf (512).
+// (The class test is written as the compare instruction itself: a ballot of
+// __builtin_amdgcn_classf is lowered through a select and a second compare.)
 __device__ __forceinline__ uint64_t silu_f32_redo_lanes(float g, float v) {
     const uint32_t m = (__float_as_uint(v) + 0x8010u) & 0xFFFFu;
-    // v not normal: |v| below the smallest normal (zero, subnormal; NaN
-    // compares false) or not below infinity
-    const float av = fabsf(v);
-    return __builtin_amdgcn_ballot_w64(!(g >= -87.0f)) | __builtin_amdgcn_ballot_w64(!(av >= 0x1p-126f)) |
-           __builtin_amdgcn_ballot_w64(!(av < __builtin_inff())) | __builtin_amdgcn_ballot_w64(m <= 32u);
+    uint64_t not_normal;
+    asm("v_cmp_class_f32_e64 %0, %1, %2" : "=s"(not_normal) : "v"(v), "s"(759u));
+    return __builtin_amdgcn_ballot_w64(!(g >= -87.0f)) | not_normal | __builtin_amdgcn_ballot_w64(m <= 32u);
 }
 
 // The float64 evaluation. Where 1 + e^-g rounds to 1 (g above about 36.7)

@@ -500,9 +500,12 @@ void gemm_kernel(GemmParams p) {
                     constexpr int RS = NT / 64;                   // row step of a thread
                     // optional tap of the rounded gate | up values (same rows,
                     // gate pair at column col, up pair at I + col)
-                    uint32_t* tap = p.gu_tap ? reinterpret_cast<uint32_t*>(
-                                                   p.gu_tap + (int64_t)(row_start + r0) * 2 * p.I + col)
-                                             : nullptr;
+                    // (has_tap is a kernel argument's test: a scalar branch, not a
+                    // per-lane pointer test around every tap store)
+                    const bool has_tap = p.gu_tap != nullptr;
+                    uint32_t* tap = has_tap ? reinterpret_cast<uint32_t*>(
+                                                  p.gu_tap + (int64_t)(row_start + r0) * 2 * p.I + col)
+                                            : nullptr;
                     const int64_t tstep = (int64_t)RS * p.I;      // RS rows of 2I bf16, in 4-byte units
                     int r = r0;
                     for (; r + 3 * RS < rows; r += 4 * RS, dst += 4 * dstep) {
@@ -514,12 +517,12 @@ void gemm_kernel(GemmParams p) {
                             u[2 * k] = bf16_to_f32(w[0] >> 16);
                             g[2 * k + 1] = bf16_to_f32(w[1] & 0xFFFFu);
                             u[2 * k + 1] = bf16_to_f32(w[1] >> 16);
-                            if (tap) {
+                            if (has_tap) {
                                 tap[k * tstep] = (w[0] & 0xFFFFu) | (w[1] << 16);
                                 tap[k * tstep + p.I / 2] = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
                             }
                         }
-                        if (tap) tap += 4 * tstep;
+                        if (has_tap) tap += 4 * tstep;
                         // lanes with an element float32 cannot decide, as a
                         // wave mask (scalar ORs of the compare masks)
                         uint64_t redo = 0;
@@ -555,7 +558,7 @@ void gemm_kernel(GemmParams p) {
                     }
                     for (; r < rows; r += RS, dst += dstep) {
                         const u32x2 w = *reinterpret_cast<const u32x2*>(gu + r * GU_LD + 2 * cp);
-                        if (tap) {
+                        if (has_tap) {
                             tap[0] = (w[0] & 0xFFFFu) | (w[1] << 16);
                             tap[p.I / 2] = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
                             tap += tstep;
