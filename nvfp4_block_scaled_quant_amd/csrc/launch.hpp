@@ -144,7 +144,7 @@ constexpr int64_t kSmallQuantMax = 1 << 17;   // elements: larger inputs take th
 // pre-pass provides.
 constexpr int64_t kRouteChunk = 4096;
 constexpr int64_t kRouteMaxChunks = 64;
-constexpr int kRouteMaxPartials = 256;
+constexpr int kRouteMaxPartials = 1024;
 int64_t route_chunk(int64_t S);
 // number of partial maxima the pre-pass writes for n activation values
 int route_amax_partials(int64_t n);

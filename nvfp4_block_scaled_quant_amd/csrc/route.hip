@@ -35,7 +35,9 @@ constexpr int kPreThreads = 256;   // threads of the pre-pass work-groups
 // magnitude bits, partial[b]); work-groups from n_amax on count the expert ids
 // of one chunk of C slots each (wg_counts[g][e], ids outside [0, E) not
 // counted). Partials instead of one atomic slot: the readers take the maximum
-// of at most 256 words, and nothing needs zeroing first.
+// of at most kRouteMaxPartials (1,024) words, and nothing needs zeroing
+// first. (At the prefill shape 1,024 work-groups instead of 256 took the
+// routing stage from 44.5 to 42.8 us: more loads in flight.)
 __global__ __launch_bounds__(kPreThreads) void route_prepass_kernel(
     const uint16_t* __restrict__ x, int64_t n, int n_amax, uint32_t* __restrict__ partial,
     const int32_t* __restrict__ ids, int64_t S, int E, int64_t C, int32_t* __restrict__ wg_counts) {

@@ -167,6 +167,17 @@ def test_routing_chunks(nv, T, H, I, E, k, skip):
     assert g["counts"].sum() == ((L["ids"] >= 0) & (L["ids"] < E)).sum()
 
 
+# the largest expert count the routing supports (512), on the weight-streaming
+# path (8,000 slots <= 16 per expert) and the tiled one with chunked routing
+# (48,000 slots, top-16), and top-k equal to E (every token to every expert)
+@pytest.mark.parametrize("T,H,I,E,k", [(1000, 128, 64, 512, 8), (3000, 128, 32, 512, 16),
+                                       (200, 256, 128, 32, 32)])
+def test_max_experts_and_topk(nv, T, H, I, E, k):
+    cfg = W.small_layer(f"maxE{E}k{k}", T=T, H=H, I=I, E=E, topk=k, seed=E + k)
+    g, _, _ = compare_layer(nv, make_layer(cfg), f"max experts T{T} E{E} k{k}")
+    assert g["counts"].sum() == T * k
+
+
 def test_skipped_ids_and_empty_experts(nv):
     cfg = W.small_layer("skip", T=90, H=256, I=128, E=6, topk=3, seed=9)
     L = make_layer(cfg)
