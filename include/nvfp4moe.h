@@ -238,7 +238,11 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *   2. route: one slot per (t, j) whose id topk_ids[t][j] is in [0, E);
  *      slots with other ids are skipped and contribute nothing
  *   3. L1: gate_up = bf16((gs1 * w13_alpha[e]) * xq[t] @ w13[e])   (S, 2I)
- *   4. act = bf16(silu(gate) * up) in float32, silu(z) = z / (1 + exp(-z));
+ *   4. act = bf16(silu(gate) * up), silu(z) = z / (1 + exp(-z)), rounded to
+ *      nearest-even from the float64 value of that formula (computed in
+ *      float32 where float32 decides the same rounding; where 1 + exp(-gate)
+ *      is 1 in float64 the product is first moved one float64 step toward
+ *      zero, as the exact value lies just inside it);
  *      quantize all valid slots' act rows -> aq, asf, gs2 (one gs2)
  *   5. L2: o[s] = (gs2 * w2_alpha[e]) * aq[s] @ w2[e] in float32, then
  *      y[t] = bf16( sum_j topk_weights[t][j] * o[slot(t, j)] ), float32, j order
@@ -255,6 +259,12 @@ int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,
  *   H % 16 == 0, I % 16 == 0, 1 <= topk <= E, T >= 0; each of
  *   2I * pitch_q(H), H * pitch_q(I), T * pitch_h(H), T * topk * pitch_h(I)
  *   below 2^31 (32-bit buffer offsets), else NVFP4_ESHAPE.
+ *
+ * Kernels: batches of at most 16 valid slots per expert on average take
+ * weight-streaming GEMMs whose LDS holds a 16-row tile of the activation
+ * (so H and I up to about 17,000); other batches, and larger H or I, take
+ * the tiled GEMMs, whose LDS use does not depend on K. The choice is made on
+ * the host from the shapes alone.
  *
  * Workspace: nvfp4_moe_workspace(T, H, I, E, topk) bytes, 256-byte aligned.
  * The intermediates stay in the workspace after the call; their byte offsets

@@ -250,6 +250,19 @@ def test_moe_workspace_layout_is_consistent(nv):
         nv.moe_workspace_size(8, 7168, 3072, 48, 49)
 
 
+def test_weight_streaming_path_stops_at_its_lds_limit(nv):
+    # a decode-size batch (8 tokens, top-8 of 48) takes the weight-streaming
+    # GEMMs while a 16-row activation tile fits their LDS (K up to 17,024);
+    # above that it takes the tiled GEMMs, whose workspace also holds the f16
+    # copies of x (T rows of pitch_h(H)) and act (S rows of pitch_h(I))
+    T, E, k = 8, 48, 8
+    for H0, I0, H1, I1 in [(17024, 256, 17040, 256), (256, 17024, 256, 17040)]:
+        a = nv.moe_workspace_size(T, H0, I0, E, k)
+        b = nv.moe_workspace_size(T, H1, I1, E, k)
+        f16 = T * 4 * nv.operand_pitches(H1)[0] + T * k * 4 * nv.operand_pitches(I1)[0]
+        assert b - a >= f16, (H1, I1, b - a, f16)     # one K step more alone adds a few KB
+
+
 def test_binding_requires_device_tensors(nv):
     import torch
     with pytest.raises(TypeError):
