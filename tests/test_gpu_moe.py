@@ -149,6 +149,14 @@ def test_small_batch_shapes(nv, T, H, I, E, k):
     compare_layer(nv, make_layer(cfg), f"small-batch T{T} H{H} I{I} E{E} k{k}")
 
 
+# small batches whose H or I is beyond what the weight-streaming kernels'
+# LDS holds (K up to 17,024) take the tiled GEMMs
+@pytest.mark.parametrize("T,H,I,E,k", [(4, 17040, 32, 2, 1), (5, 64, 17040, 2, 2)])
+def test_small_batch_beyond_streaming_lds(nv, T, H, I, E, k):
+    cfg = W.small_layer(f"bigK{H}x{I}", T=T, H=H, I=I, E=E, topk=k, seed=H + I)
+    compare_layer(nv, make_layer(cfg), f"small batch, big K: T{T} H{H} I{I}")
+
+
 # batches above one routing chunk (4096 slots) are routed by one work-group
 # per chunk after a counting pre-pass: one slot past a chunk, three chunks
 # with skipped ids on the chunk boundaries, and enough slots (264,000) for the
