@@ -45,7 +45,8 @@
 // takes tile 8 (s / ntn) + x, N-tile s % ntn: all N-tiles of one tile run on
 // one XCD, at about the same time, and read its A rows through one L2. Tiles
 // come from a device-built list (expert, first sorted row, row count), each
-// expert's full tiles followed by its partial one; the grid is sized for the worst
+// expert's full tiles followed by its partial one (partial tiles of at most
+// half the rows at the end of the list); the grid is sized for the worst
 // case and idle work-groups leave at once, so the host never waits for
 // routing counts. The dense GEMM has no tile list and few tiles (a 256-row
 // M is 24 tiles at N = 6144): its work-groups go in plain order, and when its

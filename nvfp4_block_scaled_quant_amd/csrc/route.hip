@@ -150,6 +150,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     int32_t* gbase = off + E + 1;                    // this chunk's first row per expert, past off
     int32_t* wcnt = gbase + E;                       // [kWaves][E]: counts, then running positions
     __shared__ int32_t tile_base[kMaxExperts + 1];   // first tile of each expert
+    __shared__ int32_t part_pos[kMaxExperts];        // list position of a short partial tile, or -1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -214,34 +215,47 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     // exclusive scans of counts and of tiles per expert: wave 0, 64 experts
     // at a time, shuffle-based inclusive scans within the wave. The tile list
     // holds the experts in order, each with its full BM-row tiles and then its
-    // partial one. So every round of GEMM work-groups mixes full and partial
-    // (shorter) tiles, and the rounds drift apart: the work-groups do not all
-    // store their results and load their next tiles at the same moment, which
-    // measured 2-3% faster on both grouped GEMMs than all full tiles first
-    // (one long round of equal tiles after another).
+    // partial one, except partial tiles of at most BM / 2 rows, which go to
+    // the end of the list (in expert order). So every round of GEMM
+    // work-groups mixes full and partial (shorter) tiles, and the rounds
+    // drift apart: the work-groups do not all store their results and load
+    // their next tiles at the same moment (2-3% faster on both grouped GEMMs
+    // at the prefill shape than all full tiles first, one long round of equal
+    // tiles after another), while the shortest tiles make the last round
+    // short (3% faster on a skewed routing whose partial tiles are mostly of
+    // one or two row blocks).
     if (wave == 0) {
-        int acc = 0, tacc = 0;
+        int acc = 0, tacc = 0, sacc = 0;
         for (int e0 = 0; e0 < E; e0 += 64) {
             const int e = e0 + lane;
             const int c = (e < E) ? cnt[e] : 0;
-            const int nt = (c + BM - 1) / BM;
-            int ic = c, jt = nt;
+            const int r = c % BM;
+            const bool short_part = r > 0 && r <= BM / 2;     // partial tile of at most half the rows
+            const int nt = (c + BM - 1) / BM - (short_part ? 1 : 0);
+            const int ns = short_part ? 1 : 0;
+            int ic = c, jt = nt, js = ns;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
-                const int uc = __shfl_up(ic, d), ut = __shfl_up(jt, d);
-                if (lane >= d) { ic += uc; jt += ut; }
+                const int uc = __shfl_up(ic, d), ut = __shfl_up(jt, d), us = __shfl_up(js, d);
+                if (lane >= d) { ic += uc; jt += ut; js += us; }
             }
             if (e < E) {
                 off[e] = acc + ic - c;
                 tile_base[e] = tacc + jt - nt;
+                part_pos[e] = short_part ? sacc + js - 1 : -1;   // rank among short partials, for now
             }
             acc += __shfl(ic, 63);
             tacc += __shfl(jt, 63);
+            sacc += __shfl(js, 63);
+        }
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            if (e < E && part_pos[e] >= 0) part_pos[e] += tacc;   // after all other tiles
         }
         if (lane == 0) {
             off[E] = acc;
             tile_base[E] = tacc;
-            if (g == 0) *num_tiles = tacc;
+            if (g == 0) *num_tiles = tacc + sacc;
         }
     }
     __syncthreads();
@@ -256,7 +270,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
                 t.row_start = off[e] + i * BM;
                 t.row_count = min(BM, cnt[e] - i * BM);
                 t.pad = 0;
-                tiles[tile_base[e] + i] = t;
+                if (i == nt - 1 && part_pos[e] >= 0) tiles[part_pos[e]] = t;
+                else tiles[tile_base[e] + i] = t;
             }
         }
     }
