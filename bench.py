@@ -222,11 +222,13 @@ def time_decode(nv, weights, steps, routings=8, graph=True):
             "finite": dfin}
 
 
-def time_decode_graph(nv, weights, replays=400, routings=8):
-    """The decode batch captured in HIP graphs: one graph per seeded routing,
-    each one nvfp4_moe_forward_noalloc call (the allocation-free entry point,
-    workspace in the library's static scratch), replayed round-robin; timed
-    with events on torch's current stream. Returns microseconds per step."""
+def time_decode_graph(nv, weights, replays=50, routings=8):
+    """The decode batch captured in one HIP graph: the eight seeded routings'
+    nvfp4_moe_forward_noalloc calls (the allocation-free entry point,
+    workspace in the library's static scratch) one after another, as a decode
+    loop would capture a run of layers; the graph is replayed `replays`
+    times and timed with events on torch's current stream. Returns
+    microseconds per layer call."""
     import dataclasses
     import torch
     import workloads as W
@@ -237,22 +239,20 @@ def time_decode_graph(nv, weights, replays=400, routings=8):
               for r in range(routings)]
     nv.moe_forward_noalloc(x, *routes[0], *weights, y=y)      # set-up outside the capture
     torch.cuda.synchronize()
-    graphs = []
-    for ids, wts in routes:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for ids, wts in routes:
             nv.moe_forward_noalloc(x, ids, wts, *weights, y=y)
-        graphs.append(g)
-    for i in range(2 * routings):
-        graphs[i % routings].replay()
+    for _ in range(3):
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(replays):
-        graphs[i % routings].replay()
+    for _ in range(replays):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / replays
+    return e0.elapsed_time(e1) * 1e3 / (replays * routings)
 
 
 def time_skewed(nv, weights, steps, warmup):
