@@ -224,6 +224,35 @@ def test_repeat_is_bit_identical(nv):
     assert all((y == g["ys"][0]).all() for y in g["ys"])
 
 
+def test_concurrent_streams(nv):
+    # the library keeps no per-call state outside the workspace: two layers,
+    # each with its own workspace, issued on two streams (default priority)
+    # so that their kernels may overlap, give what they give one at a time
+    import torch
+    from conftest import to_dev, to_host
+    from helpers import gpu_packed_weights
+    runs = []
+    for name, T, seed in (("cs1", 700, 61), ("cs2", 40, 62)):     # tiled and weight-streaming paths
+        L = make_layer(W.small_layer(name, T=T, H=512, I=256, E=8, topk=4, seed=seed))
+        pw = gpu_packed_weights(nv, L)
+        d = {k: to_dev(L[k]) for k in ("x", "ids", "wts")}
+        args = (d["x"], d["ids"], d["wts"], pw["w13"], pw["w13_sf"], pw["w13a"], pw["w2"], pw["w2_sf"], pw["w2a"])
+        ref = to_host(nv.moe_forward(*args))
+        ws = torch.empty((nv.moe_workspace_size(T, 512, 256, 8, 4),), dtype=torch.uint8, device="cuda")
+        runs.append((args, ref, ws))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for rep in range(4):
+        for i, (args, ref, ws) in enumerate(runs):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(nv.moe_forward(*args, workspace=ws))
+    torch.cuda.synchronize()
+    for i, (args, ref, ws) in enumerate(runs):
+        for y in outs[i]:
+            assert (to_host(y) == ref).all(), f"stream {i}"
+
+
 @pytest.mark.parametrize("static", [False, True])
 def test_repeat_is_bit_identical_large_x(nv, static):
     # x above 128K elements: amax pass, then the quantization in the routing
