@@ -6,7 +6,7 @@ Stages as the pages list them (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline"):
    one global scale gs1 over all of x;
 2. token-to-expert permutation: one slot per (token t, choice j) whose expert id
    lies in [0, E); ids outside that range are skipped (the pages do not define
-   them; this is the reading taken, see DESIGN.md);
+   them; this is the reading taken);
 3. L1 GEMM of each slot's quantized row against w13[e] = [gate; up] with
    alpha = gs1 * w13_alpha[e]; gate is the first I output columns, up the last I
    (src commit log, gate/up interleave removal);
@@ -16,18 +16,19 @@ Stages as the pages list them (NVFP4 MegaMoE Debug Log, "NVFP4 MoE Pipeline"):
    of the L2 rows back to their tokens:
    y[t] = sum_j topk_weights[t, j] * out[t, j] in j order.
 
-Rounding points (the pages print bf16-looking intermediates and say "bf16 out";
-readings in the design doc): gate_up is rounded to bf16 before SiLU (R1); act is
-rounded to bf16 once (R2); nothing between the L2 sum and y is rounded except
-the single final bf16 rounding of y (R3). Everything else here is float64, and
-SiLU(z) = z / (1 + exp(-z)).
+Rounding points (the pages print bf16-looking intermediates and a bf16
+output; these are the readings taken): gate_up is rounded to bf16 before SiLU
+(R1); act is rounded to bf16 once (R2); nothing between the L2 sum and y is
+rounded except the single final bf16 rounding of y (R3). Everything else here
+is float64, and SiLU(z) = z / (1 + exp(-z)).
 
 Parity: each stage is pinned through the modules it calls (formats, quantize,
-gemm). The layer's end-to-end values have no published expected value (the
-pages never reach a correct layer output): PARITY UNPINNED end to end; the
-composition is checked by the invariants in tests/test_oracle_moe.py
-(gate/up split, per-expert alpha, skipped slots, slot-order independence, the
-pure-Python twin on the tiny layer).
+gemm). The pages never reach a correct layer output, so no published value
+pins the layer end to end; instead a layer worked out by hand
+(tests/test_oracle_closed_form.py: constant inputs, every quantization exact,
+y = 5760) pins it, and the composition is checked by the invariants in
+tests/test_oracle_moe.py (gate/up split, per-expert alpha, skipped slots,
+slot-order independence, the pure-Python twin on the tiny layer).
 """
 import numpy as np
 

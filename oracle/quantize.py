@@ -12,7 +12,7 @@ quantizer fix and E4M3 `.view` fix):
 4. packing       element 2j in the low nibble, element 2j+1 in the high one.
 
 The pages leave the arithmetic open. This oracle takes the plainest reading and
-every GPU path must follow the same one (the readings are listed in the design doc):
+every GPU path must follow the same one:
 
 * all of it is IEEE float32 with round-to-nearest-even, no fused multiply-add,
   in exactly this order: gs = fl(amax / 2688); six_gs = fl(6 * gs);

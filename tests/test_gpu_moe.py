@@ -224,6 +224,21 @@ def test_repeat_is_bit_identical(nv):
     assert all((y == g["ys"][0]).all() for y in g["ys"])
 
 
+def test_layer_closed_form(nv):
+    # the constant layer of test_oracle_closed_form: y = 5760 everywhere, by
+    # hand; the GPU gets it exactly (and the intermediates the hand values)
+    from oracle.formats import bf16_to_f32
+    from test_oracle_closed_form import _layer
+    x, ids, wts, w13q, w13sf, w13a, w2q, w2sf, w2a = _layer()
+    L = dict(x=x, ids=ids, wts=wts, w13q=w13q, w13sf=w13sf, w13a=w13a, w2q=w2q, w2sf=w2sf, w2a=w2a)
+    g = run_gpu_layer(nv, L)
+    assert (bf16_to_f32(g["y"]) == 5760.0).all(), np.unique(bf16_to_f32(g["y"]))
+    act = bf16_to_f32(g["act"]).astype(np.float64)
+    slot = g["sorted_slot"][:act.shape[0]]
+    assert (act[slot % 2 == 0] == 73728.0).all() and (act[slot % 2 == 1] == 36864.0).all()
+    assert g["gs2"] == np.float32(73728.0) / np.float32(2688.0)
+
+
 def test_concurrent_streams(nv):
     # the library keeps no per-call state outside the workspace: two layers,
     # each with its own workspace, issued on two streams (default priority)
