@@ -163,8 +163,10 @@ def time_layer(nv, cfg, weights, steps, warmup, events_in_loop=True, variant=Non
         torch.cuda.synchronize()
     per = [ev.elapsed_ms() for ev in events]
     stage_ms = {k: float(np.mean([p[k] for p in per])) for k in per[0]}
+    # device time of each step with events: first event to last
+    step_ms = [float(sum(p.values())) for p in per]
     ok = bool(torch.isfinite(y.float()).all().item())
-    return (t1 - t0) * 1e3 / steps, stage_ms, s_valid, ids_np, ok
+    return (t1 - t0) * 1e3 / steps, stage_ms, s_valid, ids_np, ok, step_ms
 
 
 def time_router(nv, cfg, launches=200):
@@ -209,7 +211,7 @@ def time_decode(nv, weights, steps, routings=8, graph=True):
     bytes are the routings' mean algorithmic weight bytes."""
     import workloads as W
     dcfg = W.DECODE
-    dms, dstage, _, dids, dfin = time_layer(nv, dcfg, weights, steps, 5, events_in_loop=False,
+    dms, dstage, _, dids, dfin, _ = time_layer(nv, dcfg, weights, steps, 5, events_in_loop=False,
                                             routings=routings)
     nbytes, touched = decode_bytes(dcfg, dids)
     g_us = time_decode_graph(nv, weights, routings=routings) if graph else None
@@ -265,7 +267,7 @@ def time_skewed(nv, weights, steps, warmup):
     w13, w13sf, _, w2, w2sf, _ = weights
     a13, a2 = W.alphas_loguniform(scfg)
     sw = (w13, w13sf, torch.from_numpy(a13).cuda(), w2, w2sf, torch.from_numpy(a2).cuda())
-    ms, stage, s_valid, ids_np, fin = time_layer(nv, scfg, sw, steps, warmup)
+    ms, stage, s_valid, ids_np, fin, step_ms = time_layer(nv, scfg, sw, steps, warmup)
     import numpy as np
     counts = np.bincount(ids_np[0].ravel(), minlength=scfg.E)
     l1_flops = 2.0 * s_valid * scfg.H * 2 * scfg.I
@@ -274,7 +276,9 @@ def time_skewed(nv, weights, steps, warmup):
             "eff_tflops": 6.0 * s_valid * scfg.H * scfg.I / (ms * 1e-3) / 1e12,
             "l1_f16_peak_frac": l1_flops / (stage["l1"] * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
             "l2_f16_peak_frac": l1_flops / 2 / (stage["l2"] * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
-            "stage_ms": stage, "empty_experts": int((counts == 0).sum()),
+            "stage_ms": stage,
+            "step_ms_device": {"median": float(np.median(step_ms)), "min": float(np.min(step_ms))},
+            "empty_experts": int((counts == 0).sum()),
             "hottest_expert_slot_share": float(counts.max() / counts.sum()), "finite": fin}
 
 
@@ -412,6 +416,7 @@ def main():
         print(f"bench.py: the layer is measured on one GPU's share of experts; --gpus {args.gpus} "
               f"is not supported (only --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -439,10 +444,10 @@ def main():
         print(json.dumps(time_dense_gemm(nv)), flush=True)
         return
     if args.only == "prefill":
-        ms, stage_ms, _, _, _ = time_layer(nv, cfg, weights, args.steps, args.warmup)
+        ms, stage_ms, _, _, _, _ = time_layer(nv, cfg, weights, args.steps, args.warmup)
         print(json.dumps({"workload": "prefill", "ms_per_step": ms, "stage_ms": stage_ms}), flush=True)
         return
-    ms, stage_ms, s_valid, ids_np, finite = time_layer(nv, cfg, weights, args.steps, args.warmup)
+    ms, stage_ms, s_valid, ids_np, finite, step_ms = time_layer(nv, cfg, weights, args.steps, args.warmup)
     flops = 6.0 * s_valid * cfg.H * cfg.I
     l1_flops = 2.0 * s_valid * cfg.H * 2 * cfg.I
     l1_tflops = l1_flops / (stage_ms["l1"] * 1e-3) / 1e12
@@ -474,6 +479,8 @@ def main():
         "eff_tflops": flops / (ms * 1e-3) / 1e12,
         "f16_peak_frac_layer": flops / (ms * 1e-3) / 1e12 / PEAK_F16_MFMA_TFLOPS,
         "stage_ms": stage_ms,
+        "step_ms_device": {"median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
+                           "note": "per timed step, first to last stage event on the library's stream"},
         "l2_gemm": {"kernel": "L2 grouped GEMM (gemm_kernel<2>)", "achieved_tflops": l2_tflops,
                     "f16_peak_frac": l2_tflops / PEAK_F16_MFMA_TFLOPS},
         "roofline": {"bound": "mfma", "kernel": "L1 grouped GEMM (gemm_kernel<1>)",
@@ -489,11 +496,11 @@ def main():
     # extensions beyond the five stages, measured on the same prefill batch
     ext = {"router_us": {c.name: time_router(nv, c) for c in (W.PREFILL, W.SKEWED)}}
     for variant in ("static_x", "per_half"):
-        vms, vstage, _, _, vfin = time_layer(nv, cfg, weights, 10, 3, variant=variant)
+        vms, vstage, _, _, vfin, _ = time_layer(nv, cfg, weights, 10, 3, variant=variant)
         ext[variant] = {"ms_per_step": vms, "stage_ms": vstage, "finite": vfin}
     out["extensions"] = ext
     # the other configurations of the workload recipe, each measured the same way
-    out["skewed"] = time_skewed(nv, weights, max(5, args.steps // 2), 2)
+    out["skewed"] = time_skewed(nv, weights, args.steps, 3)
     out["dense_gemm"] = time_dense_gemm(nv)
     out["vendor_f16_gemm"] = vendor_f16_gemm()
     if not args.no_decode:
