@@ -35,7 +35,8 @@ def _run(nv, aq, asf, ags, bq, bsf, balpha):
                                    (300, 512, 1024), (257, 48, 7168), (64, 6144, 128),
                                    (513, 784, 896), (160, 256, 512), (100, 512, 256),
                                    (420, 384, 1024), (5, 48, 144), (33, 272, 7184),
-                                   (300, 256, 16), (64, 96, 80), (17, 64, 208), (2048, 512, 256)])
+                                   (300, 256, 16), (64, 96, 80), (17, 64, 208), (2048, 512, 256),
+                                   (64, 256, 32768), (8, 16, 65536 + 16)])
 def test_gemm_random(nv, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     out = _run(nv, *ops)
