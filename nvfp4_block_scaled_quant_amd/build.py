@@ -60,7 +60,25 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    build_capi_check(cc)
     return OUT
+
+
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "closed_form.cpp")
+CAPI_BIN = os.path.join(ROOT, "tests", "capi", "closed_form")
+
+
+def build_capi_check(cc):
+    """The C-ABI check program of the GPU tests (host code only: it calls the
+    library through include/nvfp4moe.h, linked against the in-tree .so)."""
+    if not os.path.exists(CAPI_SRC):
+        return
+    cmd = [cc, "-O2", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", CAPI_SRC, "-o", CAPI_BIN + ".tmp",
+           f"-L{PKG}", "-lnvfp4moe", "-Wl,-rpath,$ORIGIN/../../nvfp4_block_scaled_quant_amd"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C-ABI check program failed to build:\n{r.stdout}\n{r.stderr}")
+    os.replace(CAPI_BIN + ".tmp", CAPI_BIN)
 
 
 if __name__ == "__main__":
