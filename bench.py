@@ -385,15 +385,9 @@ def calibrate_copy():
         del a, b
 
 
-def vendor_f16_gemm(n=8192, reps=20):
-    """torch.matmul (hipBLASLt) on contiguous n x n x n f16 operands: what the
-    vendor's own f16 GEMM reaches on this GPU at the clock the chip holds
-    under full MFMA load. Context for the L1/L2 fractions, not the peak."""
+def _vendor_rate(a, b, flop, reps):
     import torch
-    g = torch.Generator(device="cuda").manual_seed(5)
-    a = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
-    b = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
-    c = torch.empty((n, n), device="cuda", dtype=torch.float16)
+    c = torch.matmul(a, b)
     for _ in range(5):
         torch.matmul(a, b, out=c)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -404,10 +398,51 @@ def vendor_f16_gemm(n=8192, reps=20):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    tf = 2.0 * n ** 3 / (us * 1e-6) / 1e12
-    del a, b, c
-    return {"shape": f"{n} x {n} x {n} f16, f32 accumulate", "us_per_call": us, "tflops": tf,
-            "f16_peak_frac": tf / PEAK_F16_MFMA_TFLOPS}
+    del c
+    tf = flop / (us * 1e-6) / 1e12
+    return {"us_per_call": us, "tflops": tf, "f16_peak_frac": tf / PEAK_F16_MFMA_TFLOPS}
+
+
+def _exact_f16(nv, x_bf16):
+    """The exact f16 values code * E4M3 scale of the NVFP4 quantization of the
+    rows of x (global scale left out, as in the GEMMs' f16 operands)."""
+    import torch
+    q, sf, _ = nv.quantize(x_bf16)
+    lut = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6], device=q.device)
+    codes = torch.stack([lut[(q & 15).long()], lut[(q >> 4).long()]], dim=-1).reshape(x_bf16.shape[0], -1)
+    return (codes * sf.view(torch.float8_e4m3fn).float().repeat_interleave(16, dim=1)).half()
+
+
+def vendor_f16_gemm(nv, reps=20):
+    """torch.matmul (hipBLASLt) f16 GEMMs as context for the L1/L2 fractions,
+    not the peak: (1) n x n x n on normal-distributed f16 data; (2) the L1
+    GEMM's flops as one dense GEMM (M = T * topk rows of the quantized layer
+    input, each token's row repeated topk times; N = 2I; K = H; one expert's
+    quantized w13 as B, K-major like the packed weights) on the exact f16
+    values of the NVFP4 operands. The operand values change the power the
+    matrix cores draw and so the clock the chip holds under its power limit."""
+    import torch
+    import workloads as W
+    cfg = W.PREFILL
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(5)
+    n = 8192
+    a = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.float16, generator=g)
+    out["square_normal"] = {"shape": f"{n} x {n} x {n}, normal f16 data, f32 accumulate",
+                            **_vendor_rate(a, b, 2.0 * n ** 3, reps)}
+    del a, b
+    x = to_dev(W.activations(cfg))
+    a = _exact_f16(nv, x).repeat_interleave(cfg.topk, dim=0).contiguous()
+    w13_bf16, _ = W.expert_weights_bf16(cfg, 0)
+    bt = _exact_f16(nv, to_dev(w13_bf16).t().contiguous())             # (2I, H): B, K-major
+    M, K, N = a.shape[0], a.shape[1], bt.shape[0]
+    out["l1_shape_nvfp4_values"] = {
+        "shape": f"{M} x {N} x {K} (M x N x K), exact f16 values of NVFP4 operands, B K-major, f32 accumulate",
+        **_vendor_rate(a, bt.t(), 2.0 * M * N * K, reps)}
+    del a, bt, x
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -424,11 +459,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.only == "vendor-gemm":
-        print(json.dumps(vendor_f16_gemm()), flush=True)
-        return
     import nvfp4_block_scaled_quant_amd as nv
     import workloads as W
+    if args.only == "vendor-gemm":
+        print(json.dumps(vendor_f16_gemm(nv)), flush=True)
+        return
 
     cfg = W.PREFILL
     t_setup = time.perf_counter()
@@ -502,7 +537,7 @@ def main():
     # the other configurations of the workload recipe, each measured the same way
     out["skewed"] = time_skewed(nv, weights, args.steps, 3)
     out["dense_gemm"] = time_dense_gemm(nv)
-    out["vendor_f16_gemm"] = vendor_f16_gemm()
+    out["vendor_f16_gemm"] = vendor_f16_gemm(nv)
     if not args.no_decode:
         out["decode"] = time_decode(nv, weights, args.decode_steps)
     del weights
