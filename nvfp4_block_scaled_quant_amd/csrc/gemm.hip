@@ -31,8 +31,12 @@
 // 2-byte pieces; each is brought in by a 2-byte load that fills a whole LDS
 // dword, zero-extended).
 //
-// Tiling. A work-group of 4 waves computes a 256 x 256 tile; each wave owns a
-// 128 x 128 quadrant (4 x 4 tiles of 32 x 32 x 16). Lane l serves row / column
+// Tiling. A work-group of 8 waves (two per SIMD) computes a 256 x 256 tile;
+// wave w owns rows 128 (w / 4) .. +128 and columns 64 (w % 4) .. +64 (4 x 2
+// tiles of 32 x 32 x 16, 128 accumulator registers). With two waves on a SIMD,
+// one wave's FP4 conversions, fragment reads and refill loads issue while the
+// other's MFMAs run (one wave per SIMD with 128 x 128 each left the matrix
+// core idle about a fifth of the loop). Lane l serves row / column
 // l % 32 and K half h = l / 32: of a 64-element step it covers elements
 // [32h, 32h + 32), and substep s (0..3) feeds the MFMA elements [32h + 8s, +8),
 // inside scale group 2h + s / 2; A and B use the same K permutation, so every
@@ -70,7 +74,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = kGemmBM;
 constexpr int BN = kGemmBN;
-constexpr int NT = 256;                 // threads per work-group
+constexpr int NT = 512;                 // threads per work-group: 8 waves, two per SIMD
 constexpr int KS = 64;                  // K elements per step
 constexpr int NSTAGE = 3;
 constexpr int A_ROW = 2 * KS;           // bytes of one f16 A row per step
@@ -105,7 +109,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem_raw[];
 
@@ -160,16 +164,16 @@ void gemm_kernel(GemmParams p) {
     __shared__ uint32_t red[NT / 64];
     auto tile = [&](auto mi_c) {
         constexpr int MI = decltype(mi_c)::value;
-        constexpr int NA = 2 * MI;              // A loads per wave and stage (8 rows each)
-        constexpr int NL = NA + 4;              // all loads per wave and stage
+        constexpr int NA = MI;                  // A loads per wave and stage (8 rows each)
+        constexpr int NL = NA + 2;              // all loads per wave and stage (+ B data, B scales)
         constexpr int kWaitStage = waitcnt_imm(NL, 0);   // all but one stage's loads done
         constexpr int kWaitAll = waitcnt_imm(0, 0);
         // VALU per MFMA in the substeps' schedules: the B conversion of one
-        // substep is 32 VALU plus the scale pairs, over its 4 * MI MFMAs; the
+        // substep is 16 VALU plus the scale pairs, over its 2 * MI MFMAs; the
         // last substep's first kFirst MFMAs cover the fragment reads
-        constexpr int kValu = MI == 4 ? 3 : MI == 3 ? 3 : MI == 2 ? 4 : 8;
-        constexpr int kFirst = MI == 1 ? 2 : 4;
-        constexpr int kValuLast = MI == 4 ? 4 : MI == 3 ? 5 : MI == 2 ? 8 : 20;
+        constexpr int kValu = MI == 4 ? 2 : MI == 3 ? 3 : MI == 2 ? 4 : 8;
+        constexpr int kFirst = MI == 4 ? 3 : MI == 3 ? 2 : 1;
+        constexpr int kValuLast = MI == 4 ? 4 : MI == 3 ? 5 : MI == 2 ? 7 : 20;
 
         // ---- buffer resources and per-lane DMA offsets ---------------------------
         const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.ah, p.a_rows * lda);
@@ -183,17 +187,17 @@ void gemm_kernel(GemmParams p) {
         };
         auto b_src = [&](int vc) -> int64_t {       // weight row (output column) of virtual column vc
             if (MODE == kGemmL1) {
-                const int w = vc >> 7, r = vc & 127;
-                const int64_t base = (int64_t)nt * 128 + 64 * w + (r & 63);
+                const int w = vc >> 6, r = vc & 63;
+                const int64_t base = (int64_t)nt * 128 + 32 * w + (r & 31);
                 if (base >= p.I) return 0;
-                return (r < 64) ? base : p.I + base;
+                return (r < 32) ? base : p.I + base;
             }
             const int64_t c = (int64_t)nt * BN + vc;
             return c < N ? c : 0;
         };
         // A: load u (0 .. 8 MI - 1) fills LDS bytes [1024 u, +1024) of the A
         // region: rows 8u + lane / 8, physical chunk lane % 8. Wave w issues
-        // u = NA w + t.
+        // u = NA w + t (NA = MI: the 8 waves cover the 64 MI rows).
         // (fixed size: the host pass of the compiler drops the kernel when a
         // nested lambda captures an array whose size depends on MI)
         uint32_t a_off[8];
@@ -203,17 +207,16 @@ void gemm_kernel(GemmParams p) {
             const int chunk = (lane & 7) ^ ((row >> 1) & 7);
             a_off[t] = (uint32_t)(a_src(row) * lda + 16 * chunk);
         }
-        // B: load v = 2w + t fills rows 32v + lane / 2, physical chunk lane % 2.
-        // B scales: load v = 2w + t fills dword 64v + lane = row (64v + lane) / 2,
+        // B: wave w's load fills rows 32w + lane / 2, physical chunk lane % 2.
+        // B scales: wave w's load fills dword 64w + lane = row (64w + lane) / 2,
         // pair lane % 2 of the half step's two.
-        uint32_t b_off[2], bsf_off[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int row = 32 * (2 * wave + t) + (lane >> 1);
+        uint32_t b_off, bsf_off;
+        {
+            const int row = 32 * wave + (lane >> 1);
             const int chunk = (lane & 1) ^ ((row >> 3) & 1);
-            b_off[t] = (uint32_t)wq_off(b_src(row), ldq, 16 * chunk);
+            b_off = (uint32_t)wq_off(b_src(row), ldq, 16 * chunk);
             const int64_t n = b_src(row);
-            bsf_off[t] = (uint32_t)((n >> 4) * 16 * ldwsf + (n & 15) * 32 + (lane & 1) * 8);
+            bsf_off = (uint32_t)((n >> 4) * 16 * ldwsf + (n & 15) * 32 + (lane & 1) * 8);
         }
 
         // 64-element steps: all of K, or this work-group's chunk [kb, kb + nk)
@@ -224,22 +227,22 @@ void gemm_kernel(GemmParams p) {
         const int kb = split ? chunk * kper : 0;
         const int nk = split ? min(nk_all, kb + kper) - kb : nk_all;
         // ---- main loop ---------------------------------------------------------
-        const int wm = wave >> 1, wn = wave & 1;
+        const int wm = wave >> 2, wn = wave & 3;
         const int l32 = lane & 31, h = lane >> 5;
 
-        float16_t acc[MI][4];
+        float16_t acc[MI][2];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        // Fragment rows are wm * 32 MI + 32 i + l32 (A) and wn * 128 + 32 j + l32
+        // Fragment rows are wm * 32 MI + 32 i + l32 (A) and wn * 64 + 32 j + l32
         // (B): the 32 i / 32 j parts do not change the swizzles, which then
         // depend on the lane alone. The per-lane offsets within a stage are
         // formed once; the fragments' row offsets are the reads' immediates.
-        const uint32_t a_row = (uint32_t)(wm * (32 * MI) + l32), b_row = (uint32_t)(wn * 128 + l32);
+        const uint32_t a_row = (uint32_t)(wm * (32 * MI) + l32), b_row = (uint32_t)(wn * 64 + l32);
         const int sw_a = (l32 >> 1) & 7;
         uint32_t off_a[4];
 #pragma unroll
@@ -248,10 +251,10 @@ void gemm_kernel(GemmParams p) {
         const uint32_t off_bsf = A_BYTES + B_BYTES + b_row * 8 + 4 * h;
 
         half8_t fa[2][MI];      // A operands of substep s in fa[s & 1]
-        u32x4 fb[4];            // packed B of the step: dword s = substep s
-        uint32_t sb[4];         // B scale pair of the step (2 bytes)
-        half8_t hb[2][4];       // converted B operands of substep s in hb[s & 1]
-        half2_t spb[4];         // scale pairs of the current group of two substeps
+        u32x4 fb[2];            // packed B of the step: dword s = substep s
+        uint32_t sb[2];         // B scale pair of the step (2 bytes)
+        half8_t hb[2][2];       // converted B operands of substep s in hb[s & 1]
+        half2_t spb[2];         // scale pairs of the current group of two substeps
         auto read_a = [&](int st, int s, half8_t (&dst)[MI]) {
             const uint8_t* pa = smem_raw + st * STAGE_BYTES + off_a[s];
 #pragma unroll
@@ -260,55 +263,48 @@ void gemm_kernel(GemmParams p) {
         auto read_b = [&](int st) {
             const uint8_t* base = smem_raw + st * STAGE_BYTES;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 fb[j] = *reinterpret_cast<const u32x4*>(base + off_b + j * 32 * B_ROW);
                 sb[j] = *reinterpret_cast<const uint32_t*>(base + off_bsf + j * 32 * 8);
             }
         };
-        auto deq_b = [&](int s, half8_t (&dst)[4]) {
+        auto deq_b = [&](int s, half8_t (&dst)[2]) {
             if ((s & 1) == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu);
+                for (int j = 0; j < 2; ++j) spb[j] = scale_pair((sb[j] >> (8 * (s >> 1))) & 0xFFu);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dst[j] = dequant8(fb[j][s], spb[j]);
+            for (int j = 0; j < 2; ++j) dst[j] = dequant8(fb[j][s], spb[j]);
         };
 
-        // load j (0..3) of part t of the DMA of stage ks (none when that part
-        // has fewer loads): part t < 2 holds A loads t MI .. t MI + MI - 1,
-        // part 2 the two B loads and the two scale loads
-        auto issue_one = [&](int ksr, int st, int t, int j) {
+        // slot q (0..5) of the DMA of stage ks: slots 0 .. MI-1 are this wave's
+        // A loads, slot MI its B load, slot MI + 1 its B scale load
+        auto issue_one = [&](int ksr, int st, int q) {
             const int ks = kb + ksr;                   // absolute step
             uint8_t* base = smem_raw + st * STAGE_BYTES;
-            if (t < 2) {
-                if (j < MI)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        ra, (lds_void*)(base + (NA * wave + t * MI + j) * 1024), 16, a_off[t * MI + j],
-                        (uint32_t)ks * A_ROW, 0, 0);
-            } else if (j < 2) {
+            if (q < MI) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rb, (lds_void*)(base + A_BYTES + (2 * wave + j) * 1024), 16, b_off[j],
-                    (uint32_t)ks * kWqHalf, 0, 0);
-            } else {
+                    ra, (lds_void*)(base + (NA * wave + q) * 1024), 16, a_off[q], (uint32_t)ks * A_ROW, 0, 0);
+            } else if (q == MI) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_void*)(base + A_BYTES + wave * 1024), 16, b_off, (uint32_t)ks * kWqHalf, 0, 0);
+            } else if (q == MI + 1) {
                 // half step ks of K step kst = ks / 2: pairs 2 (ks % 2) + {0, 1}
                 const int kst = ks >> 1;
                 const uint32_t ksb = (uint32_t)((kst >> 2) * kWsfQuad + (kst & 3) * 2 + (ks & 1) * 16);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rbsf, (lds_void*)(base + A_BYTES + B_BYTES + (2 * wave + j - 2) * 256), 2, bsf_off[j - 2],
-                    ksb, 0, 0);
+                    rbsf, (lds_void*)(base + A_BYTES + B_BYTES + wave * 256), 2, bsf_off, ksb, 0, 0);
             }
         };
 
         auto issue_stage = [&](int ks, int st) {
 #pragma unroll
-            for (int t = 0; t < 3; ++t)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) issue_one(ks, st, t, j);
+            for (int q = 0; q < 6; ++q) issue_one(ks, st, q);
         };
 
-        // One K step in four substeps. Substeps 0..2 run as four chunks, one
+        // One K step in four substeps. Substeps 0..2 run as two chunks, one
         // per B column block j: its MI MFMAs, the conversion of its operand of
-        // the next substep, and one load of the refill of stage ks+2 (the
+        // the next substep, and one load slot of the refill of stage ks+2 (the
         // loads, issued back to back, stall the wave's instruction stream).
         // Substep 3 starts with the wait for this wave's DMA of stage ks+1 and
         // the barrier (the other waves' DMA of it is then visible, and the
@@ -328,17 +324,17 @@ void gemm_kernel(GemmParams p) {
                 read_a(st, s + 1, fa[(s + 1) & 1]);
                 if (s == 1) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) spb[j] = scale_pair((sb[j] >> 8) & 0xFFu);
+                    for (int j = 0; j < 2; ++j) spb[j] = scale_pair((sb[j] >> 8) & 0xFFu);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 2; ++j) {
 #pragma unroll
                     for (int i = 0; i < MI; ++i)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[s & 1][i], hb[s & 1][j],
                                                                             acc[i][j], 0, 0, 0);
                     hb[(s + 1) & 1][j] = dequant8(fb[j][s + 1], spb[j]);
-                    if (PH == 0) issue_one(ks + NSTAGE - 1, sr, s, j);
+                    if (PH == 0) issue_one(ks + NSTAGE - 1, sr, 2 * s + j);
 #pragma unroll
                     for (int i = 0; i < MI; ++i) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
@@ -360,15 +356,15 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1][i], hb[1][j], acc[i][j], 0, 0, 0);
             if (PH < 2) {
                 deq_b(0, hb[0]);
                 // the fragment reads land under the first MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, MI + 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, MI + 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, kFirst, 0);
 #pragma unroll
-                for (int k = 0; k < 4 * MI - kFirst; ++k) {
+                for (int k = 0; k < 2 * MI - kFirst; ++k) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, kValuLast, 0);
                 }
@@ -426,7 +422,7 @@ void gemm_kernel(GemmParams p) {
                 for (int g = 0; g < 4; ++g) {
                     const int local = wm * (32 * MI) + 32 * i + 8 * g + 4 * h + m;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < 2; ++j) {
                         float v0 = scale * acc[i][j][4 * g], v1 = scale * acc[i][j][4 * g + 1];
                         float v2 = scale * acc[i][j][4 * g + 2], v3 = scale * acc[i][j][4 * g + 3];
                         // stage 1 (lanes m, m ^ 1): even lanes take the partner's
@@ -444,7 +440,7 @@ void gemm_kernel(GemmParams p) {
                         const float r2b = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
                             __builtin_bit_cast(int, s2b), 0x4E, 0xF, 0xF, false));
                         if (upper) { v0 = r2a; v1 = r2b; } else { v2 = r2a; v3 = r2b; }
-                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + 4 * (l32 >> 2);
+                        const int64_t col = (int64_t)nt * BN + wn * 64 + 32 * j + 4 * (l32 >> 2);
                         if (local < row_count && col < N)   // N % 16 == 0: four columns are in or out together
                             *reinterpret_cast<float4_t*>(out + (row_start + local) * N + col) =
                                 (float4_t){v0, v1, v2, v3};
@@ -453,14 +449,14 @@ void gemm_kernel(GemmParams p) {
             }
         };
         // ---- epilogue ------------------------------------------------------------
-        // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the quadrant
+        // acc[i][j][r] = D[row 32i + 8(r/4) + 4h + (r%4)][col 32j + l32] of the wave's part
         // L1 with per-half weight scales: gate columns take alpha, up alpha_up
         const int ast = (MODE == kGemmL1 && p.alpha_stride > 1) ? 2 : 1;
         const float alpha = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast];
         if (MODE == kGemmL1) {
             const float alpha_up = p.a_gs[0] * p.b_alpha[(int64_t)expert * ast + ast - 1];
-            // gate = virtual columns [0, 64) of the quadrant (blocks 0, 1), up = [64, 128).
-            // All four waves stage the rounded (gate, up) pairs of the whole
+            // gate = the wave's block 0 (32 act columns), up = block 1.
+            // All eight waves stage the rounded (gate, up) pairs of the whole
             // tile (64 * MI rows x 128 act columns) in the now idle LDS, rows
             // padded to 130 words (the two lane halves' rows, four apart, then
             // fall in different banks; 8-byte reads stay aligned); then all
@@ -474,16 +470,14 @@ void gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int row = wm * (32 * MI) + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                        const int col = wn * 64 + 32 * j + l32;
-                        gu[row * GU_LD + col] = pack_bf16x2_rne(alpha * acc[i][j][r], alpha_up * acc[i][j + 2][r]);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * (32 * MI) + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int col = wn * 32 + l32;
+                    gu[row * GU_LD + col] = pack_bf16x2_rne(alpha * acc[i][0][r], alpha_up * acc[i][1][r]);
+                }
             __syncthreads();
             // each thread: one pair of adjacent act columns (one 4-byte store)
-            // in rows tid / 64, + 4, ...; a wave covers one row (256 contiguous
+            // in rows tid / 64, + NT / 64, ...; a wave covers one row (256 contiguous
             // bytes), so the row bound is wave-uniform
             {
                 const int cp = tid & 63;
@@ -491,14 +485,14 @@ void gemm_kernel(GemmParams p) {
                 if (col < p.I) {
                     const int r0 = tid >> 6;
                     uint32_t* dst = reinterpret_cast<uint32_t*>(p.out_bf16 + (int64_t)(row_start + r0) * p.I + col);
-                    const int64_t dstep = 2 * p.I;                // 4 rows, in 4-byte units
+                    constexpr int RS = NT / 64;                   // row step of a thread
+                    const int64_t dstep = (int64_t)RS * (p.I / 2);    // RS rows of I bf16, in 4-byte units
                     const int rows = min(row_count, 64 * MI);
                     // Four rows per pass: their eight float32 SiLUs form one
-                    // branch-free block of independent chains (one wave per SIMD
-                    // has nothing else to hide the exp / rcp latencies), and the
-                    // elements float32 cannot decide are redone in float64 after
-                    // it, behind one branch that is rarely taken.
-                    constexpr int RS = NT / 64;                   // row step of a thread
+                    // branch-free block of independent chains that hide the exp
+                    // and rcp latencies, and the elements float32 cannot decide
+                    // are redone in float64 after it, behind one branch that is
+                    // rarely taken.
                     // optional tap of the rounded gate | up values (same rows,
                     // gate pair at column col, up pair at I + col)
                     // (has_tap is a kernel argument's test: a scalar branch, not a
@@ -576,7 +570,8 @@ void gemm_kernel(GemmParams p) {
             if (lane == 0) red[wave] = amax_bits;
             __syncthreads();
             if (tid == 0) {
-                uint32_t m = max(max(red[0], red[1]), max(red[2], red[3]));
+                uint32_t m = red[0];
+                for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
                 atomicMax(p.amax_slot, m << 16);
             }
         } else if (MODE == kGemmL2) {
@@ -592,8 +587,8 @@ void gemm_kernel(GemmParams p) {
                     if (local >= row_count) continue;
                     const int64_t prow = row_start + local;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int64_t col = (int64_t)nt * BN + wn * 128 + 32 * j + l32;
+                    for (int j = 0; j < 2; ++j) {
+                        const int64_t col = (int64_t)nt * BN + wn * 64 + 32 * j + l32;
                         if (col >= N) continue;
                         const float v = alpha * acc[i][j][r];
                         p.out_bf16[prow * N + col] = (uint16_t)f32_to_bf16_rne(v);
