@@ -5,10 +5,13 @@
 // With a handful of rows per expert the layer is bound by reading the expert
 // weights from HBM once, so the kernel is built around the weight stream:
 //
-// * A work-group owns one 16-row tile and a slab of 4 x 16 NB weight rows
-//   (output columns; NB = 10 for L2; for L1, NB = 8: 4 x 64 gate columns and
-//   the matching up columns). Its 16 A rows are staged once in LDS, still packed, while the
-//   first weight loads are already in flight.
+// * A work-group of 8 waves (two per SIMD, one work-group per CU) owns one
+//   16-row tile and a slab of 8 x 16 NB weight rows (output columns; NB = 10
+//   for L2; for L1, NB = 8: 8 x 64 gate columns and the matching up columns).
+//   Its 16 A rows are staged once in LDS, still packed, while the first weight
+//   loads are already in flight. (With 4 waves, two work-groups shared a CU and
+//   the one dispatched second finished about a third later, alone on the CU
+//   for the tail; one 8-wave work-group per CU streams evenly to the end.)
 // * Each wave streams its own 16 NB weight rows over the whole of K, two K
 //   steps in flight, with non-temporal loads (the weights are read once),
 //   and finishes its outputs by itself (no cross-wave reduction). Per
@@ -43,14 +46,14 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int NT = 256;
-constexpr int NW = NT / 64;       // waves per work-group
+constexpr int NT = 512;
+constexpr int NW = NT / 64;       // waves per work-group (two per SIMD)
 constexpr int SM = 16;            // rows per tile
 // MFMA column blocks per lane (weight rows 16f + c of the wave's 16 * NB):
-// L1 4 gate + 4 up blocks; L2 10 blocks, so that a tile needs 12 work-groups
-// for 7168 output columns instead of 14 at 8 blocks: the decode batch touches
-// up to about 42 experts, and 42 x 12 work-groups still fit the 512 that the
-// GPU holds at once (two per CU), where 37 x 14 already need a second round
+// L1 4 gate + 4 up blocks; L2 10 blocks, so that a tile needs 6 work-groups
+// for 7168 output columns instead of 7 at 8 blocks: the decode batch touches
+// up to about 42 experts, and 42 x 6 work-groups still fit the 256 that the
+// GPU holds at once (one per CU), where 37 x 7 already need a second round
 // whose few work-groups each take a whole stream's latency-bound time
 template <int MODE> constexpr int kNB = MODE == kGemmL1 ? 8 : 10;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -321,7 +324,11 @@ void skinny_kernel(GemmParams p) {
         amax_bits = wave_max_u32(amax_bits);
         if (lane == 0) wred[wave] = amax_bits;
         __syncthreads();
-        if (tid == 0) atomicMax(p.amax_slot, max(max(wred[0], wred[1]), max(wred[2], wred[3])) << 16);
+        if (tid == 0) {
+            uint32_t m = wred[0];
+            for (int w = 1; w < NW; ++w) m = max(m, wred[w]);
+            atomicMax(p.amax_slot, m << 16);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
