@@ -217,6 +217,7 @@ def time_decode(nv, weights, steps, routings=8, graph=True):
     g_us = time_decode_graph(nv, weights, routings=routings) if graph else None
     return {"workload": "decode", "tokens": dcfg.T, "routings": routings, "us_per_step": dms * 1e3,
             "graph_us_per_step": g_us, "graph_GBps": nbytes / (g_us * 1e-6) / 1e9 if g_us else None,
+            "graph_hbm_frac": nbytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBPS if g_us else None,
             "touched_experts_mean": touched, "algorithmic_bytes_mean": nbytes,
             "GBps": nbytes / (dms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
