@@ -33,7 +33,8 @@
 //
 // Tiling. A work-group of 8 waves (two per SIMD) computes a 256 x 256 tile;
 // wave w owns rows 128 (w / 4) .. +128 and columns 64 (w % 4) .. +64 (4 x 2
-// tiles of 32 x 32 x 16, 128 accumulator registers). With two waves on a SIMD,
+// tiles of 32 x 32 x 16, 128 accumulator registers; 32 MI rows per wave row
+// in the variants below). With two waves on a SIMD,
 // one wave's FP4 conversions, fragment reads and refill loads issue while the
 // other's MFMAs run (one wave per SIMD with 128 x 128 each left the matrix
 // core idle about a fifth of the loop). Lane l serves row / column
