@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void quant_cols_kernel(
     const int64_t groups = K / 16;
     const int64_t per = groups * N;
     const uint16_t* we = w + e * K * N;
-    if (blockIdx.x == 0 && threadIdx.x < parts)
+    if (blockIdx.x == 0 && (int)threadIdx.x < parts)
         alpha[e * parts + threadIdx.x] = make_scales(__uint_as_float(amax_slots[e * parts + threadIdx.x])).gs;
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < per;
          i += (int64_t)gridDim.x * kThreads) {
