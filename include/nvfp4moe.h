@@ -222,10 +222,11 @@ int nvfp4_prepack_weights(const uint8_t* w, const uint8_t* w_sf, int64_t E, int6
  * Workspace: nvfp4_gemm_workspace(M, N, K) bytes, 256-byte aligned. It
  * receives A in its exact f16 form (e2m1 * e4m3 per element, M rows of
  * pitch_h(K) bytes padded with zeros to whole 128-element steps), the operand
- * the matrix cores read, and, when the output tiles (256 x 256) would fill
- * less than half the GPU, the float32 partial sums of the chunks K is cut
- * into (one M x N plane per chunk, added in chunk order before alpha and the
- * bf16 rounding). nvfp4_gemm_workspace returns 0 for invalid sizes.
+ * the matrix cores read, and, when 256 x 256 output tiles would fill less
+ * than half the GPU, the float32 partial sums of the chunks K is cut into
+ * (the tiles are then 128 x 256; one M x N plane per chunk, added in chunk
+ * order before alpha and the bf16 rounding). nvfp4_gemm_workspace returns 0
+ * for invalid sizes.
  * ------------------------------------------------------------------------ */
 size_t nvfp4_gemm_workspace(int64_t M, int64_t N, int64_t K);
 int nvfp4_gemm(const uint8_t* aq, const uint8_t* asf, const float* a_gs,

@@ -54,11 +54,13 @@
 // half the rows at the end of the list); the grid is sized for the worst
 // case and idle work-groups leave at once, so the host never waits for
 // routing counts. The dense GEMM has no tile list and few tiles (a 256-row
-// M is 24 tiles at N = 6144): its work-groups go in plain order, and when its
-// tiles would fill less than half the GPU the K steps are cut into chunks, one
-// work-group per (tile, chunk) with at most one work-group per CU, each
-// writing float32 partial sums that a second kernel adds in chunk order
-// before the one bf16 rounding. Invalid rows and columns of a tile read a valid row instead
+// M is 24 tiles at N = 6144): its work-groups go in plain order, and when
+// 256-row tiles would fill less than half the GPU it takes 128-row tiles
+// (twice the tiles) and cuts the K steps into chunks, one work-group per
+// (tile, chunk) with at most one work-group per CU, each writing float32
+// partial sums that a second kernel adds in chunk order before the one bf16
+// rounding (the half-height tiles halve the chunks, and so the partial sums
+// written and read back). Invalid rows and columns of a tile read a valid row instead
 // (their results are never stored). Rows are read in whole steps: the padding
 // of a partial last step is zero in both operands (the quantizers and the
 // weight prepack write it as zeros), so it adds nothing.
@@ -127,7 +129,7 @@ void gemm_kernel(GemmParams p) {
     // the XCD order would put on one XCD.
     int tile_idx, nt, chunk = 0;
     if (MODE == kGemmDense) {
-        const int mt = (int)((p.M + BM - 1) / BM);
+        const int mt = (int)((p.M + dense_tile_rows(p.M, N) - 1) / dense_tile_rows(p.M, N));
         tile_idx = blockIdx.x % mt;
         const int rest = blockIdx.x / mt;
         nt = rest % ntn;
@@ -142,8 +144,9 @@ void gemm_kernel(GemmParams p) {
     int expert, row_start, row_count;
     if (MODE == kGemmDense) {
         expert = 0;
-        row_start = tile_idx * BM;
-        row_count = (int)min((int64_t)BM, p.M - row_start);
+        const int dbm = (int)dense_tile_rows(p.M, N);
+        row_start = tile_idx * dbm;
+        row_count = (int)min((int64_t)dbm, p.M - row_start);
         if (row_count <= 0) return;
     } else {
         if (tile_idx >= p.max_tiles) return;      // the grid covers whole groups of 8 tiles
@@ -607,7 +610,8 @@ void gemm_kernel(GemmParams p) {
 template <int MODE>
 hipError_t launch_mode(const GemmParams& p, hipStream_t s) {
     const int64_t ntn = (MODE == kGemmL1) ? (p.I + 127) / 128 : (p.N + BN - 1) / BN;
-    const int64_t mt = (MODE == kGemmDense) ? (p.M + BM - 1) / BM : p.max_tiles;
+    const int64_t mt = (MODE == kGemmDense) ? (p.M + dense_tile_rows(p.M, p.N) - 1) / dense_tile_rows(p.M, p.N)
+                                            : p.max_tiles;
     // grouped: whole groups of 8 tiles (one per XCD); dense: every (tile, N-tile, K chunk)
     const int64_t grid = (MODE == kGemmDense) ? mt * ntn * p.ksplit : (mt + 7) / 8 * 8 * ntn;
     if (grid <= 0) return hipSuccess;
@@ -654,7 +658,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }  // namespace
 
 int dense_ksplit(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = (M + BM - 1) / BM * ((N + BN - 1) / BN);
+    const int64_t tiles = (M + dense_tile_rows(M, N) - 1) / dense_tile_rows(M, N) * ((N + BN - 1) / BN);
     const int64_t nk = pitch_q(K) / 32;
     if (tiles <= 0 || tiles >= 128 || nk < 8) return 1;
     // at most one work-group per CU: a second round would double the time

@@ -222,6 +222,14 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // chunk at least 4 K steps and none empty.
 int dense_ksplit(int64_t M, int64_t N, int64_t K);
 
+// Rows per dense GEMM tile: 128 when 256-row tiles would fill less than half
+// the GPU (the split-K regime: half-height tiles double the tiles and halve
+// the K chunks, and with them the partial sums written and read back), else 256.
+__host__ __device__ inline int64_t dense_tile_rows(int64_t M, int64_t N) {
+    const int64_t t256 = (M + kGemmBM - 1) / kGemmBM * ((N + kGemmBN - 1) / kGemmBN);
+    return t256 < 128 ? kGemmBM / 2 : kGemmBM;
+}
+
 // out[m][n] = bf16((a_gs[0] * b_alpha[0]) * sum over chunks c, in order, of
 // partial[c][m][n]) for (M, N), N % 4 == 0.
 hipError_t launch_splitk_reduce(const float* partial, int ksplit, int64_t M, int64_t N, const float* a_gs,

@@ -103,10 +103,11 @@ def test_gemm_argument_errors(nv):
     # the workspace holds A as f16, rows padded to whole 128-element steps
     assert ws(4, 16, 144) == 4 * 512                    # K = 144 pads to 256 elements: 512 bytes a row
     assert ws(3, 16, 16) == 3 * 256                      # K = 16: one 128-element step, 256 bytes a row
-    # 24 output tiles of 256 x 256: K's 112 64-element steps go in 10 chunks
-    # of up to 12 (240 work-groups, at most one per CU), each chunk with an
-    # fp32 partial-sum plane of M x N after the f16 A
-    assert ws(256, 6144, 7168) == 256 * 7168 * 2 + 10 * 256 * 6144 * 4
+    # 256-row tiles would be only 24: the dense GEMM takes 48 tiles of 128 x 256
+    # and cuts K's 112 64-element steps into 5 chunks of up to 23 (240
+    # work-groups, at most one per CU), each chunk with an fp32 partial-sum
+    # plane of M x N after the f16 A
+    assert ws(256, 6144, 7168) == 256 * 7168 * 2 + 5 * 256 * 6144 * 4
     assert ws(4096, 6144, 7168) == 4096 * 7168 * 2      # 384 tiles: no split
     assert ws(4, 16, 24) == 0 and ws(-1, 16, 128) == 0
     assert call(args, 4, 16, 144, nbytes=ws(4, 16, 144) - 1) == 3
