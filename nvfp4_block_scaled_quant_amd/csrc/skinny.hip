@@ -9,7 +9,8 @@
 //   16-row tile and a slab of 8 x 16 NB weight rows (output columns; NB = 10
 //   for L2; for L1, NB = 8: 8 x 64 gate columns and the matching up columns).
 //   Its 16 A rows are staged once in LDS, still packed, while the first weight
-//   loads are already in flight. (With 4 waves, two work-groups shared a CU and
+//   loads are already in flight (the A loads are issued first: loads return
+//   in order). (With 4 waves, two work-groups shared a CU and
 //   the one dispatched second finished about a third later, alone on the CU
 //   for the tail; one 8-wave work-group per CU streams evenly to the end.)
 // * Each wave streams its own 16 NB weight rows over the whole of K, two K
@@ -169,6 +170,45 @@ void skinny_kernel(GemmParams p) {
         if (MODE == kGemmL1) my_src = p.a_gather[my_src] / p.topk;
     }
 
+    // ---- stage the tile's A rows (packed, pitch ldq) and scales into LDS ------
+    uint8_t* sA = smem;                              // [16][ldq + 16]
+    const int a_pitch = (int)ldq + 16;               // 16-byte skew between rows
+    uint8_t* sAsf = smem + SM * a_pitch;             // [16][ldsf]
+    __shared__ int64_t src_row[SM];
+    if (tid < SM) src_row[tid] = my_src;
+    __syncthreads();
+    // scales in 8-byte pieces (groups beyond K are masked in compute()), data
+    // in 16-byte pieces; the first pass's loads are issued before the first
+    // two weight steps, so that (returns being in order) they do not wait for
+    // the weights
+    const int cs = (int)(ldsf / 8), ns = SM * cs;
+    const int cq = (int)(ldq / 16), nq = SM * cq;
+    auto load_sf = [&](int i) -> u32x2 {
+        const int r = i / cs, j = i - r * cs;
+        return (i < ns && src_row[r] >= 0) ? *reinterpret_cast<const u32x2*>(p.asf + src_row[r] * ldsf + 8 * j)
+                                           : (u32x2){0u, 0u};
+    };
+    auto load_q = [&](int i) -> u32x4 {
+        const int r = i / cq, j = i - r * cq;
+        return (i < nq && src_row[r] >= 0) ? *reinterpret_cast<const u32x4*>(p.aq + src_row[r] * ldq + 16 * j)
+                                           : (u32x4){0u, 0u, 0u, 0u};
+    };
+    auto store_sf = [&](int i, u32x2 v) {
+        const int r = i / cs, j = i - r * cs;
+        if (i < ns) *reinterpret_cast<u32x2*>(sAsf + r * ldsf + 8 * j) = v;
+    };
+    auto store_q = [&](int i, u32x4 v) {
+        const int r = i / cq, j = i - r * cq;
+        if (i < nq) *reinterpret_cast<u32x4*>(sA + r * a_pitch + 16 * j) = v;
+    };
+    u32x2 vs[4];
+    u32x4 vq[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) vs[u] = load_sf(tid + u * NT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vq[u] = load_q(tid + u * NT);
+    __builtin_amdgcn_sched_barrier(0);
+
     // The first two weight steps are in flight while A is staged. Both loads
     // are issued on every path into the main loop, in this order (a wave with
     // fewer steps loads step 0 again), so that the compiler's waits at the
@@ -179,52 +219,22 @@ void skinny_kernel(GemmParams p) {
     load(nsteps > 1 ? 1 : 0, r1, kOld);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- stage the tile's A rows (packed, pitch ldq) and scales into LDS ------
-    uint8_t* sA = smem;                              // [16][ldq + 16]
-    const int a_pitch = (int)ldq + 16;               // 16-byte skew between rows
-    uint8_t* sAsf = smem + SM * a_pitch;             // [16][ldsf]
-    __shared__ int64_t src_row[SM];
-    if (tid < SM) src_row[tid] = my_src;
-    __syncthreads();
-    {
-        // scales: 8-byte pieces (groups beyond K are masked in compute())
-        const int cs = (int)(ldsf / 8), ns = SM * cs;
-        for (int i0 = tid; i0 < ns; i0 += 4 * NT) {
-            u32x2 v[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * NT;
-                const int r = i / cs, j = i - r * cs;
-                v[u] = (u32x2){0u, 0u};
-                if (i < ns && src_row[r] >= 0)
-                    v[u] = *reinterpret_cast<const u32x2*>(p.asf + src_row[r] * ldsf + 8 * j);
-            }
+    for (int u = 0; u < 4; ++u) store_sf(tid + u * NT, vs[u]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * NT;
-                const int r = i / cs, j = i - r * cs;
-                if (i < ns) *reinterpret_cast<u32x2*>(sAsf + r * ldsf + 8 * j) = v[u];
-            }
-        }
-        // data: 16-byte pieces, eight loads in flight per thread
-        const int cq = (int)(ldq / 16), nq = SM * cq;
-        for (int i0 = tid; i0 < nq; i0 += 8 * NT) {
-            u32x4 v[8];
+    for (int u = 0; u < 8; ++u) store_q(tid + u * NT, vq[u]);
+    // further passes (long rows), eight loads in flight per thread
+    for (int i0 = tid + 4 * NT; i0 < ns; i0 += 4 * NT) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * NT;
-                const int r = i / cq, j = i - r * cq;
-                v[u] = (u32x4){0u, 0u, 0u, 0u};
-                if (i < nq && src_row[r] >= 0)
-                    v[u] = *reinterpret_cast<const u32x4*>(p.aq + src_row[r] * ldq + 16 * j);
-            }
+        for (int u = 0; u < 4; ++u) vs[u] = load_sf(i0 + u * NT);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * NT;
-                const int r = i / cq, j = i - r * cq;
-                if (i < nq) *reinterpret_cast<u32x4*>(sA + r * a_pitch + 16 * j) = v[u];
-            }
-        }
+        for (int u = 0; u < 4; ++u) store_sf(i0 + u * NT, vs[u]);
+    }
+    for (int i0 = tid + 8 * NT; i0 < nq; i0 += 8 * NT) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vq[u] = load_q(i0 + u * NT);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) store_q(i0 + u * NT, vq[u]);
     }
     __syncthreads();
 
