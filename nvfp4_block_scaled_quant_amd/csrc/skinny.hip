@@ -9,8 +9,8 @@
 //   16-row tile and a slab of 8 x 16 NB weight rows (output columns; NB = 10
 //   for L2; for L1, NB = 8: 8 x 64 gate columns and the matching up columns).
 //   Its 16 A rows are staged once in LDS, still packed, while the first weight
-//   loads are already in flight (the A loads are issued first: loads return
-//   in order). (With 4 waves, two work-groups shared a CU and
+//   loads are already in flight (weight step 0, then the A rows, then weight
+//   step 1: loads return in order). (With 4 waves, two work-groups shared a CU and
 //   the one dispatched second finished about a third later, alone on the CU
 //   for the tail; one 8-wave work-group per CU streams evenly to the end.)
 // * Each wave streams its own 16 NB weight rows over the whole of K, two K
@@ -162,13 +162,20 @@ void skinny_kernel(GemmParams p) {
     const std::true_type kNew;
     const std::false_type kOld;
 
-    // A tensor row of each tile row (-1: none), read before the weight loads
-    // below are issued, so that waiting for it does not wait for them
+    // Loads return in order, so the prologue issues them in the order they
+    // are needed: the A tensor row of each tile row (-1: none), weight step
+    // 0, the A rows of the tile (staged into LDS below), then weight step 1.
+    // Both weight loads are issued on every path into the main loop, in this
+    // order (a wave with fewer steps loads step 0 again), so that the
+    // compiler's waits at the loop head are the ones of the steady state.
     int64_t my_src = -1;
     if (tid < SM && tid < row_count) {
         my_src = row_start + tid;
         if (MODE == kGemmL1) my_src = p.a_gather[my_src] / p.topk;
     }
+    Raw r0, r1;
+    load(0, r0, kNew);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- stage the tile's A rows (packed, pitch ldq) and scales into LDS ------
     uint8_t* sA = smem;                              // [16][ldq + 16]
@@ -178,9 +185,8 @@ void skinny_kernel(GemmParams p) {
     if (tid < SM) src_row[tid] = my_src;
     __syncthreads();
     // scales in 8-byte pieces (groups beyond K are masked in compute()), data
-    // in 16-byte pieces; the first pass's loads are issued before the first
-    // two weight steps, so that (returns being in order) they do not wait for
-    // the weights
+    // in 16-byte pieces; the first pass's loads are issued before weight step
+    // 1, so that writing them to LDS waits for step 0 only
     const int cs = (int)(ldsf / 8), ns = SM * cs;
     const int cq = (int)(ldq / 16), nq = SM * cq;
     auto load_sf = [&](int i) -> u32x2 {
@@ -209,13 +215,6 @@ void skinny_kernel(GemmParams p) {
     for (int u = 0; u < 8; ++u) vq[u] = load_q(tid + u * NT);
     __builtin_amdgcn_sched_barrier(0);
 
-    // The first two weight steps are in flight while A is staged. Both loads
-    // are issued on every path into the main loop, in this order (a wave with
-    // fewer steps loads step 0 again), so that the compiler's waits at the
-    // loop head are the ones of the steady state.
-    Raw r0, r1;
-    load(0, r0, kNew);
-    __builtin_amdgcn_sched_barrier(0);
     load(nsteps > 1 ? 1 : 0, r1, kOld);
     __builtin_amdgcn_sched_barrier(0);
 
