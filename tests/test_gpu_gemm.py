@@ -30,13 +30,15 @@ def _run(nv, aq, asf, ags, bq, bsf, balpha):
 
 
 # K not a multiple of 128 (144, 208, 80, 16, 7168 + 16): the A rows' f16 form
-# and the packed weights are padded with zeros to whole 128-element steps
+# and the packed weights are padded with zeros to whole 128-element steps. Shapes
+# whose 256-row tiles would fill less than half the GPU run 128-row tiles
+# (with K chunks, or, at 1280 x 6144, 240 tiles and no chunks)
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 32, 384), (17, 272, 640), (256, 256, 256),
                                    (300, 512, 1024), (257, 48, 7168), (64, 6144, 128),
                                    (513, 784, 896), (160, 256, 512), (100, 512, 256),
                                    (420, 384, 1024), (5, 48, 144), (33, 272, 7184),
                                    (300, 256, 16), (64, 96, 80), (17, 64, 208), (2048, 512, 256),
-                                   (64, 256, 32768), (8, 16, 65536 + 16)])
+                                   (64, 256, 32768), (8, 16, 65536 + 16), (1280, 6144, 1024)])
 def test_gemm_random(nv, M, N, K):
     ops = _operands(M, N, K, seed=M + N + K)
     out = _run(nv, *ops)

@@ -109,6 +109,12 @@ def test_gemm_argument_errors(nv):
     # plane of M x N after the f16 A
     assert ws(256, 6144, 7168) == 256 * 7168 * 2 + 5 * 256 * 6144 * 4
     assert ws(4096, 6144, 7168) == 4096 * 7168 * 2      # 384 tiles: no split
+    # 512 rows: 96 tiles of 128 x 256, 2 chunks; 1280 rows: 240 tiles of
+    # 128 x 256 fill the GPU without a split (256-row tiles would be 120);
+    # 3072 rows: 288 tiles of 256 x 256, no split
+    assert ws(512, 6144, 7168) == 512 * 7168 * 2 + 2 * 512 * 6144 * 4
+    assert ws(1280, 6144, 7168) == 1280 * 7168 * 2
+    assert ws(3072, 6144, 7168) == 3072 * 7168 * 2
     assert ws(4, 16, 24) == 0 and ws(-1, 16, 128) == 0
     assert call(args, 4, 16, 144, nbytes=ws(4, 16, 144) - 1) == 3
     assert call(args, 4, 16, 144, wsp=A16 + 64) == 3    # misaligned workspace
